@@ -1,0 +1,82 @@
+"""Shared workload cases for the tests (CPU side): inputs plus oracle results."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import oracle
+import workload as W
+
+
+def small_workloads():
+    """Cheap CPU cases covering every configuration's shape and the edge cases."""
+    cases = {}
+    cases["decode_edge_b4"] = W.make("decode_edge_b4")
+    c2 = W.make("decode_b256")
+    cases["decode_b256[6]"] = c2.subset([0, 1, 17, 100, 200, 255])
+    c3 = W.make("prefill_varlen_s64")
+    short = np.argsort(c3.lq)[:3].tolist() + [int(np.argmax(c3.lq))]
+    cases["prefill_varlen_s64[4]"] = c3.subset(short)
+    c4 = W.make("prefill_prefix_s128")
+    cases["prefill_prefix_s128[3]"] = c4.subset([0, 5, 77])
+    c5 = W.make("decode_long_b512")
+    cases["decode_long_b512[2]"] = c5.subset([int(np.argmin(c5.lk)), 3])
+    # edge cases: tiny blocks, empty and ragged contexts, every GQA group size
+    cases["decode_tiny_bs16"] = W.decode([0, 1, 15, 16, 17, 33, 64], num_q_heads=4, num_kv_heads=1,
+                                         head_dim=64, block_size=16, seed=11, name="decode_tiny_bs16")
+    cases["decode_mha_bs32"] = W.decode([31, 32, 1, 97], num_q_heads=2, num_kv_heads=2,
+                                        head_dim=128, block_size=32, seed=12, pad_tokens=3,
+                                        name="decode_mha_bs32")
+    cases["decode_g16"] = W.decode([5, 300], num_q_heads=16, num_kv_heads=1, head_dim=128,
+                                   block_size=256, seed=13, name="decode_g16")
+    cases["prefill_ragged_bs16"] = W.prefill([0, 1, 17, 40, 3], num_q_heads=4, num_kv_heads=2,
+                                             head_dim=64, block_size=16, seed=14,
+                                             name="prefill_ragged_bs16")
+    cases["prefill_hist_bs32"] = W.prefill([5, 33, 1], hist=[7, 0, 40], num_q_heads=8,
+                                           num_kv_heads=2, head_dim=128, block_size=32, seed=15,
+                                           name="prefill_hist_bs32")
+    cases["prefill_prefix_bs16"] = W.prefill([3, 20], prefix_len=32, num_q_heads=2,
+                                             num_kv_heads=1, head_dim=64, block_size=16, seed=16,
+                                             name="prefill_prefix_bs16")
+    return cases
+
+
+@functools.lru_cache(maxsize=None)
+def _cases():
+    return small_workloads()
+
+
+def case_names():
+    return list(_cases().keys())
+
+
+def get(name):
+    return _cases()[name]
+
+
+@functools.lru_cache(maxsize=None)
+def inputs(name):
+    """Host inputs (uint16 bf16 bits) and the cache images after the oracle store."""
+    w = get(name)
+    h = w.host_inputs()
+    kc, vc = oracle.store_kvcache(h["k_cache"], h["v_cache"], h["k_new"], h["v_new"],
+                                  h["slot_mapping"])
+    h["k_cache_stored"], h["v_cache_stored"] = kc, vc
+    return h
+
+
+def run_oracle(w, h, k_cache=None, v_cache=None):
+    kc = h["k_cache_stored"] if k_cache is None else k_cache
+    vc = h["v_cache_stored"] if v_cache is None else v_cache
+    if w.kind == "decode":
+        return oracle.paged_decode(h["q"], kc, vc, h["block_tables"], h["context_lens"],
+                                   w.block_size, w.scale)
+    return oracle.paged_prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["cu_seqlens_k"],
+                                h["block_tables"], w.block_size, w.scale, w.causal)
+
+
+@functools.lru_cache(maxsize=None)
+def reference(name):
+    w = get(name)
+    return run_oracle(w, inputs(name))
