@@ -1,0 +1,181 @@
+/*
+ * pagedkv.h -- C ABI of the paged KV-cache data plane for MI355X (gfx950).
+ *
+ * Three operations, as the Nano-vLLM write-ups describe the data plane:
+ *
+ *   pkv_store_kvcache             write each new token's K and V rows into the
+ *                                 block-paged cache at its slot-mapping entry
+ *   pkv_paged_decode_attention    one query token per sequence attending to its
+ *                                 whole cached history through its block table
+ *   pkv_varlen_prefill_attention  causal attention over packed variable-length
+ *                                 prompts (cu_seqlens), keys read through block
+ *                                 tables, so blocks shared by prefix caching are
+ *                                 read in place
+ *
+ * Sources: "Nano-vLLM part 1" (neutree.ai, translated on blog.itpub.net):
+ * section 4.1 (fixed-size blocks, 256 tokens by default), 4.2 (prefix caching
+ * by per-block hashes and reference counts), 4.3 (CPU control plane, GPU data
+ * plane; freed blocks are not zeroed), 5.2 (prefill packs sequences with
+ * cumulative lengths; decode passes positions and slot mappings), 5.3 (decode
+ * steps replayed as captured graphs).  "Nano-vLLM inference engine
+ * architecture" (blog.hotdry.top): the PagedAttention section (slot_mapping
+ * into a flat slot-indexed cache, the store_kvcache kernel) and the low-level
+ * optimisation section (a varlen prefill call and a KV-cache decode call).
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Pointers named as device buffers must be device memory (hipMalloc or
+ *    equivalent); bf16 buffers must be 16-byte aligned.  All bf16 tensors are
+ *    dense row-major with the shapes stated.
+ *  - KV cache layout: k_cache and v_cache are separate bf16 tensors of shape
+ *    [num_blocks * block_size, num_kv_heads, head_dim]; slot s of a cache is
+ *    row s, the token at offset o of physical block b lives in slot
+ *    b * block_size + o.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work and returns; ordering between calls is stream order.  No
+ *    call allocates device memory, synchronises, or reads device memory from
+ *    the host, so all of them may be captured into a HIP graph.
+ *  - The caller owns every buffer.  The library keeps no state apart from a
+ *    thread-local error message.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns PKV_ERR_INVALID_ARG or PKV_ERR_UNSUPPORTED and enqueues
+ *    nothing.  PKV_ERR_HIP reports a launch failure.  pkv_last_error() then
+ *    describes the failure.
+ *  - Contents of device metadata (slots, block ids, lengths) are NOT checked:
+ *    out-of-range slots or block ids, two new tokens with one slot, a context
+ *    longer than its block table, or a store into a block another sequence
+ *    reads (a shared prefix block) are undefined behaviour.
+ *  - head_dim must be 64 or 128; block_size a power of two >= 16.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,  /* null pointer, misalignment, inconsistent sizes */
+  PKV_ERR_UNSUPPORTED = 2,  /* a size this build has no kernel for */
+  PKV_ERR_HIP = 3           /* the HIP runtime refused the launch */
+} pkv_status;
+
+/*
+ * Store: for each i < num_tokens with slot_mapping[i] >= 0,
+ *   k_cache[slot_mapping[i]] = k[i]  and  v_cache[slot_mapping[i]] = v[i]
+ * (hotdry.top, PagedAttention section: new keys and values written at their
+ * slot-mapping offsets; "Nano-vLLM part 1", section 5.2: decode passes the
+ * slot mapping).  A negative slot is a padding entry and is skipped.  Rows of
+ * the cache not named by the mapping keep their contents bit for bit.
+ *
+ *   k, v          device bf16 [num_tokens, num_kv_heads, head_dim]
+ *   k_cache,
+ *   v_cache       device bf16 [num_slots, num_kv_heads, head_dim], updated in place
+ *   slot_mapping  device int32 [num_tokens]
+ * num_tokens == 0 is a no-op.
+ */
+pkv_status pkv_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cache,
+                             const int32_t* slot_mapping, int64_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
+                             void* stream);
+
+/*
+ * Workspace the decode call needs for its split-context partial results, in
+ * bytes (0 when one pass per sequence suffices).  `split_tokens` as for
+ * pkv_paged_decode_attention.  Returns SIZE_MAX for invalid sizes.
+ */
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_context_len,
+                                  int32_t split_tokens);
+
+/* The number of context tokens one workgroup covers for these sizes when
+ * split_tokens == 0 (automatic choice). */
+int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len);
+
+/*
+ * Decode attention: for each sequence b and query head h, with
+ * n = context_lens[b], g = h / (num_q_heads / num_kv_heads) and
+ * K_j, V_j the rows of kv head g at slot
+ *   block_tables[b][j / block_size] * block_size + j % block_size,
+ *   out[b][h] = sum_j softmax_j(scale * q[b][h] . K_j) * V_j,  j = 0 .. n-1
+ * ("Nano-vLLM part 1", sections 2.4, 4.1 and 5.2; hotdry.top, the KV-cache
+ * decode call).  context_lens counts the token stored for this step.  A
+ * sequence with n == 0 gets a zero row.  fp32 accumulation, bf16 result
+ * rounded to nearest even.
+ *
+ *   out           device bf16 [batch, num_q_heads, head_dim]
+ *   q             device bf16 [batch, num_q_heads, head_dim]
+ *   block_tables  device int32 [batch, max_blocks_per_seq]; entries past a
+ *                 sequence's last block are ignored (-1 by convention)
+ *   context_lens  device int32 [batch]
+ *   max_context_len  host-side bound: context_lens[b] <= max_context_len <=
+ *                 max_blocks_per_seq * block_size (sizes the launch; no device
+ *                 read).  Tokens beyond it are never visited.
+ *   split_tokens  context tokens per workgroup: 0 = automatic, else a positive
+ *                 multiple of 32.  Sequences longer than one split are
+ *                 processed in several workgroups whose partial softmax states
+ *                 are merged by log-sum-exp in a second kernel.
+ *   workspace     device buffer of at least pkv_decode_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0); scratch, contents
+ *                 undefined afterwards.
+ * batch == 0 is a no-op.  Any num_q_heads / num_kv_heads ratio is accepted.
+ */
+pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t batch,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, int32_t split_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * Variable-length prefill attention over packed sequences.  Sequence i owns
+ * query rows cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 (Lq_i of them) and key
+ * positions 0 .. Lk_i-1, Lk_i = cu_seqlens_k[i+1] - cu_seqlens_k[i], read from
+ * the cache through block_tables[i] ("Nano-vLLM part 1", section 5.2:
+ * cumulative sequence lengths; hotdry.top, the varlen prefill call).  Keys of
+ * a cached prefix are simply positions whose blocks other tables list too
+ * (section 4.2).  With causal != 0, query row r sits at absolute position
+ * (Lk_i - Lq_i) + r and attends keys 0 .. that position (so Lk_i >= Lq_i is
+ * required); otherwise it attends all Lk_i keys.  Each query row is
+ *   out[row][h] = sum_j softmax_j(scale * q[row][h] . K_j) * V_j
+ * with the kv head of h as for decode.  The K/V of every key position,
+ * including this step's tokens, must already be in the cache
+ * (pkv_store_kvcache first).  Rows that see no key get zeros.
+ *
+ *   out           device bf16 [total_q, num_q_heads, head_dim]
+ *   q             device bf16 [total_q, num_q_heads, head_dim]
+ *   cu_seqlens_q  device int32 [num_seqs + 1], cu[0] = 0, non-decreasing, cu[num_seqs] = total_q
+ *   cu_seqlens_k  device int32 [num_seqs + 1], as above over key counts
+ *   block_tables  device int32 [num_seqs, max_blocks_per_seq]
+ *   max_seqlen_q, max_seqlen_k   host-side bounds on Lq_i and Lk_i (size the
+ *                 launch; max_seqlen_k <= max_blocks_per_seq * block_size)
+ * num_seqs == 0 or total_q == 0 is a no-op.
+ */
+pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* cu_seqlens_q,
+                                        const int32_t* cu_seqlens_k,
+                                        const int32_t* block_tables, int32_t num_seqs,
+                                        int64_t total_q, int32_t max_seqlen_q,
+                                        int32_t max_seqlen_k, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_blocks_per_seq,
+                                        float scale, int32_t causal, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

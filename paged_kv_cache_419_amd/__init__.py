@@ -1,0 +1,11 @@
+"""Paged KV-cache data plane for MI355X: HIP kernels behind a C ABI.
+
+The three operations -- ``store_kvcache``, ``paged_decode_attention`` and
+``varlen_prefill_attention`` -- run in ``libpagedkv.so`` (built in-tree by
+``python -m paged_kv_cache_419_amd.build``); this package only marshals torch
+tensors into the C calls.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, PagedKVError, decode_split_tokens, decode_workspace_bytes, load,
+    paged_decode_attention, store_kvcache, varlen_prefill_attention, version,
+)

@@ -1,0 +1,245 @@
+// C ABI of the paged KV-cache data plane: argument checks, launch planning and
+// error reporting.  Nothing here allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "pagedkv.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t{1} << s) < x) ++s;
+  return s;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+pkv_status check_heads(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "head counts must be positive (q %d, kv %d)", num_q_heads,
+                num_kv_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", head_dim);
+  return PKV_OK;
+}
+
+pkv_status check_block_size(int32_t block_size) {
+  if (!pow2(block_size) || block_size < 16)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d: must be a power of two >= 16", block_size);
+  return PKV_OK;
+}
+
+int32_t resolve_split(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t split) {
+  return split > 0 ? split : pkv::decode_auto_split(batch, hq, hkv, max_ctx);
+}
+
+int32_t num_splits(int32_t max_ctx, int32_t split) {
+  const int32_t n = (max_ctx + split - 1) / split;
+  return n < 1 ? 1 : n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "pagedkv 0.1.0 gfx950"; }
+
+pkv_status pkv_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cache,
+                             const int32_t* slot_mapping, int64_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int64_t num_slots,
+                             void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
+  if (num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_kv_heads %d and head_dim %d must be positive",
+                num_kv_heads, head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", head_dim);
+  if (num_slots <= 0) return fail(PKV_ERR_INVALID_ARG, "num_slots must be positive");
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "bf16 buffers must be 16-byte aligned");
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (num_tokens > (int64_t{1} << 31) - 1 || row > (int64_t{1} << 20))
+    return fail(PKV_ERR_UNSUPPORTED, "num_tokens or row size too large");
+  return hip_status(pkv::launch_store_kvcache(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                              static_cast<int32_t>(row),
+                                              static_cast<hipStream_t>(stream)),
+                    "store_kvcache launch");
+}
+
+int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len) {
+  (void)head_dim;
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return pkv::decode_auto_split(batch, num_q_heads, num_kv_heads, max_context_len);
+}
+
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_context_len,
+                                  int32_t split_tokens) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0 || split_tokens < 0 || num_q_heads % num_kv_heads)
+    return SIZE_MAX;
+  if (batch == 0) return 0;
+  const int32_t split = resolve_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
+  const int32_t n = num_splits(max_context_len, split);
+  if (n == 1) return 0;
+  return static_cast<size_t>(batch) * num_q_heads * n * (head_dim + 2) * sizeof(float);
+}
+
+pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t batch,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, int32_t split_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch %d < 0", batch);
+  pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if ((st = check_block_size(block_size)) != PKV_OK) return st;
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (max_context_len < 0 ||
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "max_context_len %d outside [0, max_blocks_per_seq * block_size]",
+                max_context_len);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (split_tokens < 0 || split_tokens % 32)
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d: 0 or a positive multiple of 32", split_tokens);
+  if (batch == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "bf16 buffers must be 16-byte aligned");
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t head_groups = (group + 15) / 16;
+  if (batch > 65535 || static_cast<int64_t>(num_kv_heads) * head_groups > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "batch or kv-head count beyond the launch grid");
+  const int32_t split = resolve_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
+  const int32_t n = num_splits(max_context_len, split);
+  const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                 max_context_len, split_tokens);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? size_t{0} : workspace_bytes);
+  if (need > 0 && !aligned16(workspace))
+    return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = need > 0 ? static_cast<float*>(workspace) +
+                             static_cast<size_t>(batch) * num_q_heads * n * head_dim
+                       : nullptr;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.group = group;
+  a.head_groups = head_groups;
+  a.block_shift = log2i(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.split_tokens = split;
+  a.n_split = n;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(pkv::launch_paged_decode(a, static_cast<hipStream_t>(stream)),
+                    "paged_decode_attention launch");
+}
+
+pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* cu_seqlens_q,
+                                        const int32_t* cu_seqlens_k,
+                                        const int32_t* block_tables, int32_t num_seqs,
+                                        int64_t total_q, int32_t max_seqlen_q,
+                                        int32_t max_seqlen_k, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_blocks_per_seq,
+                                        float scale, int32_t causal, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size argument");
+  pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (st != PKV_OK) return st;
+  if ((st = check_block_size(block_size)) != PKV_OK) return st;
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (static_cast<int64_t>(max_seqlen_k) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "max_seqlen_k %d exceeds max_blocks_per_seq * block_size",
+                max_seqlen_k);
+  if (causal && max_seqlen_q > max_seqlen_k)
+    return fail(PKV_ERR_INVALID_ARG, "causal prefill needs max_seqlen_q <= max_seqlen_k");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "bf16 buffers must be 16-byte aligned");
+  if (total_q > (int64_t{1} << 31) - 1)
+    return fail(PKV_ERR_UNSUPPORTED, "total_q beyond 2^31 - 1 rows");
+
+  pkv::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.block_tables = block_tables;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.group = num_q_heads / num_kv_heads;
+  a.block_shift = log2i(block_size);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_seqlen_q = max_seqlen_q;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(pkv::launch_varlen_prefill(a, static_cast<hipStream_t>(stream)),
+                    "varlen_prefill_attention launch");
+}
+
+}  // extern "C"

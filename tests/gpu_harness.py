@@ -1,0 +1,73 @@
+"""Run a workload through the HIP library and the oracle (GPU tests and smoke)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_419_amd as pkv
+from workload import bf16_bits
+
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+def gpu_step(w, split_tokens: int = 0, tensors=None, store: bool = True):
+    """Store this step's new tokens, then run decode or prefill, all on the GPU."""
+    t = w.materialize("cuda") if tensors is None else tensors
+    if store:
+        pkv.store_kvcache(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+    if w.kind == "decode":
+        pkv.paged_decode_attention(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                   t["context_lens"], w.block_size, w.max_context_len, w.scale,
+                                   split_tokens)
+    else:
+        pkv.varlen_prefill_attention(out, t["q"], t["k_cache"], t["v_cache"], t["cu_seqlens_q"],
+                                     t["cu_seqlens_k"], t["block_tables"],
+                                     int(w.lq.max()) if w.num_seqs else 0,
+                                     int(w.lk.max()) if w.num_seqs else 0, w.block_size,
+                                     w.scale, w.causal)
+    torch.cuda.synchronize()
+    return t, out
+
+
+def rows_for(w, seqs):
+    """Row indices of ``out`` that belong to the given sequences, in subset order."""
+    if w.kind == "decode":
+        return np.asarray(seqs, dtype=np.int64)
+    cu = w.cu_seqlens_q
+    return np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs]).astype(np.int64)
+
+
+def oracle_for(w, seqs):
+    """fp64 oracle result for a few sequences, computed on their own compact block pool."""
+    sub = w.subset(seqs)
+    h = sub.host_inputs()
+    kc, vc = oracle.store_kvcache(h["k_cache"], h["v_cache"], h["k_new"], h["v_new"],
+                                  h["slot_mapping"])
+    if sub.kind == "decode":
+        return oracle.paged_decode(h["q"], kc, vc, h["block_tables"], h["context_lens"],
+                                   sub.block_size, sub.scale)
+    return oracle.paged_prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["cu_seqlens_k"],
+                                h["block_tables"], sub.block_size, sub.scale, sub.causal)
+
+
+def to_f64(out_rows: torch.Tensor) -> np.ndarray:
+    return oracle.bf16_to_f64(bf16_bits(out_rows))
+
+
+def compare(gpu: np.ndarray, ref: np.ndarray):
+    """Elementwise |gpu - ref| <= ATOL + RTOL * |ref|; returns (ok, max abs err, max rel err)."""
+    err = np.abs(gpu - ref)
+    ok = bool(np.all(err <= ATOL + RTOL * np.abs(ref))) and bool(np.isfinite(gpu).all())
+    rel = float((err / np.maximum(np.abs(ref), 1e-30)).max()) if err.size else 0.0
+    return ok, float(err.max()) if err.size else 0.0, rel
+
+
+def check_against_oracle(w, out: torch.Tensor, seqs):
+    ref = oracle_for(w, seqs)
+    got = to_f64(out[torch.from_numpy(rows_for(w, seqs)).to(out.device)])
+    ok, ea, er = compare(got, ref)
+    assert ok, f"{w.name}: max abs err {ea:.3e}, max rel err {er:.3e} over {len(seqs)} sequences"
+    return ea, er
