@@ -1,0 +1,254 @@
+"""Benchmark of the paged KV-cache data plane on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path over one batch: the store of the step's
+new tokens into the paged cache, then decode attention (decode workloads) or
+varlen prefill attention (prefill workloads).  Inputs are seeded synthetic
+tensors already resident in HBM.  Several identical copies of the inputs are
+rotated between steps so that a step does not find the previous step's K/V in
+L2 or the Infinity Cache.
+
+Prints one JSON line: whole-step throughput (algorithmic HBM bytes per second
+for decode, algorithmic FLOP/s for prefill), a roofline object for the
+attention kernel timed with HIP events around each launch inside the timed
+region, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode HBM GB/s (% peak) + decode tok/s; prefill TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+DEFAULT_WORKLOAD = "decode_b256"
+
+
+# ---- algorithmic work ------------------------------------------------------------------
+def store_bytes(w) -> int:
+    """Read k and v rows, write them into the cache, read the slot index."""
+    row = w.num_kv_heads * w.head_dim * 2
+    return int(w.num_new_tokens * (4 * row + 4))
+
+
+def decode_bytes(w) -> int:
+    """Each live K and V row of one kv head read once, plus Q, O, tables, lengths."""
+    kv = int(w.lk.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * 2
+    tables = sum(-(-int(n) // w.block_size) for n in w.lk) * 4 + 4 * w.num_seqs
+    return kv + qo + tables
+
+
+def prefill_flops(w) -> int:
+    """4 * d flops per visible (query, key) pair per query head."""
+    pairs = 0
+    for lq, lk in zip(w.lq.tolist(), w.lk.tolist()):
+        off = lk - lq
+        pairs += lq * off + lq * (lq + 1) // 2 if w.causal else lq * lk
+    return int(4 * w.head_dim * w.num_q_heads * pairs)
+
+
+def prefill_bytes(w) -> int:
+    qo = 2 * int(w.lq.sum()) * w.num_q_heads * w.head_dim * 2
+    kv = int(w.lk.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    return qo + kv
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_419_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_sources_sha") != kernel_sources_sha():
+        return None
+    return rec.get("kernels", {}).get(kernel, {}).get("hbm_bytes_per_launch")
+
+
+# ---- CPU baseline: the fp64 oracle on a bounded sample ----------------------------------
+def cpu_baseline(w, budget_s: float):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    rng = np.random.Generator(np.random.PCG64(17))
+    order = rng.permutation(w.num_seqs)
+    done, t_work, units = [], 0.0, 0
+    for s in order:
+        sub = w.subset([int(s)])
+        h = sub.host_inputs()  # input generation is not timed
+        t0 = time.perf_counter()
+        kc, vc = oracle.store_kvcache(h["k_cache"], h["v_cache"], h["k_new"], h["v_new"],
+                                      h["slot_mapping"])
+        if w.kind == "decode":
+            oracle.paged_decode(h["q"], kc, vc, h["block_tables"], h["context_lens"],
+                                sub.block_size, sub.scale)
+            units += decode_bytes(sub) + store_bytes(sub)
+        else:
+            oracle.paged_prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["cu_seqlens_k"],
+                                 h["block_tables"], sub.block_size, sub.scale, sub.causal)
+            units += prefill_flops(sub)
+        t_work += time.perf_counter() - t0
+        done.append(int(s))
+        if t_work >= budget_s:
+            break
+    if limiter is not None:
+        limiter.unregister()
+    if w.kind == "decode":
+        value, unit = units / t_work / 1e9, "GB/s"
+    else:
+        value, unit = units / t_work / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {w.num_seqs} sequences (store + attention, fp64 NumPy, "
+                      f"one thread), {t_work:.1f} s of oracle time; input generation untimed"}
+
+
+# ---- GPU run ----------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--replicas", type=int, default=0, help="input copies rotated (0 = auto)")
+    ap.add_argument("--split-tokens", type=int, default=0, help="decode split (0 = library's choice)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the data plane has no cross-GPU step in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_419_amd as pkv
+    import workload as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pkv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.make(args.workload)
+    decode = w.kind == "decode"
+    work_set = (decode_bytes(w) if decode else prefill_bytes(w)) + store_bytes(w)
+    reps = args.replicas or max(1, min(4, math.ceil(2.0e9 / work_set)))
+    copies = [w.materialize(dev) for _ in range(reps)]
+    outs = [torch.empty_like(c["q"]) for c in copies]
+    split = args.split_tokens
+    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                          w.max_context_len, split) if decode else 0
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    max_q = int(w.lq.max())
+    max_k = int(w.lk.max())
+
+    def store(c):
+        pkv.store_kvcache(c["k_new"], c["v_new"], c["k_cache"], c["v_cache"], c["slot_mapping"])
+
+    def attend(c, out):
+        if decode:
+            pkv.paged_decode_attention(out, c["q"], c["k_cache"], c["v_cache"], c["block_tables"],
+                                       c["context_lens"], w.block_size, w.max_context_len, w.scale,
+                                       split, workspace)
+        else:
+            pkv.varlen_prefill_attention(out, c["q"], c["k_cache"], c["v_cache"], c["cu_seqlens_q"],
+                                         c["cu_seqlens_k"], c["block_tables"], max_q, max_k,
+                                         w.block_size, w.scale, w.causal)
+
+    for i in range(args.warmup):
+        store(copies[i % reps])
+        attend(copies[i % reps], outs[i % reps])
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        c = copies[i % reps]
+        ev[i][0].record(stream)
+        store(c)
+        ev[i][1].record(stream)
+        attend(c, outs[i % reps])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    store_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms_step = total_ms / args.steps
+
+    if decode:
+        step_bytes = decode_bytes(w) + store_bytes(w)
+        value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
+        achieved = decode_bytes(w) / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+        kernel = "paged_decode_attention"
+    else:
+        value, unit = prefill_flops(w) / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+        achieved = prefill_flops(w) / (attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
+        kernel = "varlen_prefill_attention"
+    roof["traffic"] = measured_traffic(args.workload, kernel)
+    roof["kernel"] = kernel
+    roof["kernel_ms"] = attn_ms
+
+    # correctness of what was timed: one sampled sequence against the oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_harness as H
+    probe = [int(np.argmax(w.lk if decode else w.lq))]
+    H.check_against_oracle(w, outs[0], probe)
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": args.workload, "kind": w.kind, "sequences": w.num_seqs,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
+            "context_tokens": int(w.lk.sum()), "new_tokens": w.num_new_tokens,
+            "split_tokens": (split or pkv.decode_split_tokens(w.num_seqs, w.num_q_heads,
+                                                              w.num_kv_heads, w.head_dim,
+                                                              w.max_context_len)) if decode else None,
+            "input_copies_rotated": reps, "parallelism": "none (1 GPU)"},
+        "store_ms": store_ms, "attention_ms": attn_ms,
+        "roofline": roof,
+    }
+    if decode:
+        rec["decode_tok_per_s"] = w.num_seqs / (ms_step * 1e-3)
+        rec["hbm_frac"] = value / HBM_PEAK_GBS
+    else:
+        rec["mfma_frac"] = value / MFMA_BF16_PEAK_TFLOPS
+        rec["store_gbs"] = store_bytes(w) / (store_ms * 1e-3) / 1e9
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
