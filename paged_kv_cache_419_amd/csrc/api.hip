@@ -151,12 +151,17 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
     return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID_ARG, "bf16 buffers must be 16-byte aligned");
+  if (static_cast<int64_t>(num_kv_heads) * head_dim * 2 * 16 >= (int64_t{1} << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "num_kv_heads %d too large for 32-bit in-block offsets",
+                num_kv_heads);
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t head_groups = (group + 15) / 16;
-  if (batch > 65535 || static_cast<int64_t>(num_kv_heads) * head_groups > 65535)
-    return fail(PKV_ERR_UNSUPPORTED, "batch or kv-head count beyond the launch grid");
   const int32_t split = resolve_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
   const int32_t n = num_splits(max_context_len, split);
+  if (static_cast<int64_t>(batch) * num_kv_heads * head_groups * n > (int64_t{1} << 30))
+    return fail(PKV_ERR_UNSUPPORTED, "more than 2^30 decode work items");
+  if (static_cast<int64_t>(batch) * num_q_heads > (int64_t{1} << 30))
+    return fail(PKV_ERR_UNSUPPORTED, "batch * num_q_heads beyond the launch grid");
   const size_t need = pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
                                                  max_context_len, split_tokens);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))

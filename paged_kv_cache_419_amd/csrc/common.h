@@ -11,6 +11,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: workgroups go round-robin to 8 accelerator dies
 constexpr float kLog2e = 1.4426950408889634f;
 
 // D = C + A * B on one 16x16x32 bf16 MFMA tile (fp32 accumulate).
@@ -23,15 +24,32 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed pair of bf16 (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-// Two fp32 -> packed pair of bf16 (lo in bits 0..15).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+// fp32 -> bf16 bit pattern, round to nearest even.
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Raw buffer descriptor over `num_bytes` bytes at `base`.  Loads at offsets
+// past num_bytes return zeros without touching memory (hardware range check).
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data format, no swizzle
+
+__device__ __forceinline__ buffer_rsrc make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(num_bytes),
+                                           kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(buffer_rsrc r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -15,15 +15,25 @@
 // more than one split, each split writes its merged (m, l, output) to the
 // workspace and a second kernel combines the splits by log-sum-exp.
 //
+// Memory pipeline.  The kernel is bound by HBM, so each wave keeps the next
+// tile's K and V loads in flight while it computes the current one (two
+// register buffers).  A 16-token half of a tile always lies inside one cache
+// block, so it is addressed by one buffer descriptor whose base is the block's
+// slot row (64-bit, in scalar registers) and whose size is the number of live
+// tokens in the half: lanes of tokens past the context read zeros from the
+// hardware range check, never the stale (possibly NaN) contents of unused
+// slots.  Per-lane offsets are constant for the whole loop.
+//
 // Matrix cores.  Scores are computed transposed, S^T[token][head] = K Q^T, on
-// 16x16x32 bf16 MFMA tiles: K rows go straight from HBM into the A operand
-// (lane l holds 16 contiguous bytes of token row l % 16), the zero-padded query
-// heads form B.  The output lane layout of S^T is exactly the B-operand layout
-// P^T needs for O^T[d][head] = V^T P^T, so probabilities never leave their
-// lanes, and every lane owns one head's softmax state (scale factors are
-// lane-local).  V^T as the A operand needs V transposed: each wave stages its
-// 32-token V tile in a private LDS region (row-major) and reads it back
-// column-wise.  Exponentials use exp2 with scale * log2(e) folded in.
+// 16x16x32 bf16 MFMA tiles: K rows go straight from HBM into the A operand,
+// the zero-padded query heads form B.  The output lane layout of S^T is the
+// B-operand layout P^T needs for O^T[d][head] = V^T P^T, so probabilities
+// never leave their lanes and every lane owns one head's softmax state.  V^T
+// as the A operand needs V transposed: each wave writes its V tile row-major
+// into a private LDS region (rows padded to keep the transposed reads free of
+// bank conflicts) and reads it back with the gfx950 transposing LDS load
+// (ds_read_b64_tr_b16), four tokens of one column per lane and instruction.
+// Exponentials use exp2 with scale * log2(e) folded in.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,34 +47,178 @@ constexpr int kDecTile = 32;  // tokens per wave iteration: two 16-token MFMA ti
 
 template <int D>
 struct DecodeShape {
-  static constexpr int KK = D / 32;                      // MFMA k-steps over head_dim
-  static constexpr int DB = D / 16;                      // 16-row d-blocks of O^T
-  static constexpr int CH = D / 8;                       // 16-byte pieces per head row
-  static constexpr int VROW = D * 2 + 16;                // staged V row stride (bytes)
-  static constexpr int ROWS_PER_LOAD = kWave / CH;       // V rows one wave load covers
-  static constexpr int VREGS = kDecTile / ROWS_PER_LOAD; // V loads per lane per tile
+  static constexpr int KK = D / 32;                       // MFMA k-steps over head_dim
+  static constexpr int DB = D / 16;                       // 16-row d-blocks of O^T
+  static constexpr int CH = D / 8;                        // 16-byte pieces per head row
+  static constexpr int ROWS_PER_LOAD = kWave / CH;        // V rows one wave load covers
+  static constexpr int VLOADS = kDecTile / ROWS_PER_LOAD; // V loads per lane per tile
+  static constexpr int VROW = D * 2 + 32;                 // staged V row stride (bytes)
   static constexpr int LDS_STAGE = kDecWaves * kDecTile * VROW;
   static constexpr int LDS_MERGE = (2 * kDecWaves * 16 + kDecWaves * 16 * D) * 4;
   static constexpr int LDS = LDS_STAGE > LDS_MERGE ? LDS_STAGE : LDS_MERGE;
 };
 
-// k-slot t (0..7) of lane quarter q4 in a 32-token tile: tokens 4*q4+t of the
-// first 16-token half for t < 4, 16+4*q4+(t-4) of the second for t >= 4.
-__device__ __forceinline__ int tile_token(int q4, int t) {
-  return (t < 4) ? (4 * q4 + t) : (12 + 4 * q4 + t);
+// K and V registers of one 32-token tile.
+template <int D>
+struct TileRegs {
+  u32x4 k[2][DecodeShape<D>::KK];
+  u32x4 v[DecodeShape<D>::VLOADS];
+};
+
+// Block-table entries are read with scalar loads: the index is the same for
+// the whole wave and the table is never written by the kernel.
+typedef const __attribute__((address_space(4))) int32_t* gtable;
+// LDS pointers with their address space spelled out, so the compiler knows
+// the staging stores cannot touch global memory.
+typedef __attribute__((address_space(3))) unsigned char* lds_bytes;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Buffer descriptor of the 16 token rows of one kv head starting at logical
+// position j (a multiple of 16) of a sequence; `live` of them are readable
+// (0 = none: the loads return zeros and touch no memory).
+template <int D>
+__device__ __forceinline__ buffer_rsrc half_rsrc(const uint16_t* cache, gtable bt, int j, int shift,
+                                                 int64_t row_elems, int g, int live) {
+  const int bmask = (1 << shift) - 1;
+  const int64_t blk = bt[j >> shift];
+  const uint16_t* p = cache + ((blk << shift) + (j & bmask)) * row_elems + static_cast<int64_t>(g) * D;
+  return make_rsrc(p, static_cast<uint32_t>(live) * static_cast<uint32_t>(row_elems * 2));
+}
+
+// Issue the K and V loads of the tile starting at j0 (no branches: halves
+// past the context get empty descriptors whose loads return zeros).  `jsafe`
+// is a position known to lie inside the context; its block is looked up
+// instead of a block past the end.
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* kc, const uint16_t* vc,
+                                          gtable bt, int j0, int t1, int jsafe, int shift,
+                                          int64_t row_elems, int g, uint32_t koff,
+                                          const uint32_t (&voff)[DecodeShape<D>::VLOADS]) {
+  using S = DecodeShape<D>;
+  // (readfirstlane keeps these provably wave-uniform, so the descriptors stay
+  // in scalar registers)
+  const int live0 = __builtin_amdgcn_readfirstlane(max(0, min(16, t1 - j0)));
+  const int live1 = __builtin_amdgcn_readfirstlane(max(0, min(16, t1 - j0 - 16)));
+  const int ja = live0 > 0 ? j0 : jsafe;
+  const int jb = live1 > 0 ? j0 + 16 : ja;
+  const buffer_rsrc k0 = half_rsrc<D>(kc, bt, ja, shift, row_elems, g, live0);
+  const buffer_rsrc k1 = half_rsrc<D>(kc, bt, jb, shift, row_elems, g, live1);
+  const buffer_rsrc v0 = half_rsrc<D>(vc, bt, ja, shift, row_elems, g, live0);
+  const buffer_rsrc v1 = half_rsrc<D>(vc, bt, jb, shift, row_elems, g, live1);
+#pragma unroll
+  for (int kk = 0; kk < S::KK; ++kk) {
+    r.k[0][kk] = buffer_load16(k0, koff + 64 * kk);
+    r.k[1][kk] = buffer_load16(k1, koff + 64 * kk);
+  }
+#pragma unroll
+  for (int e = 0; e < S::VLOADS; ++e) {
+    const bool second = e * S::ROWS_PER_LOAD >= 16;
+    r.v[e] = buffer_load16(second ? v1 : v0, voff[e]);
+  }
+}
+
+// Transposed LDS read: lane (n16, q4) of the result holds column n16 of the
+// 4 x 16 block whose rows its 16-lane group addresses (ds_read_b64_tr_b16).
+__device__ __forceinline__ uint2 lds_read_tr16(lds_bytes p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
 }
 
 template <int D>
-__global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void compute_tile(const TileRegs<D>& r, const u32x4 (&qb)[DecodeShape<D>::KK],
+                                             f32x4 (&o)[DecodeShape<D>::DB], float& m, float& lsum,
+                                             lds_bytes vst, int j0, int t1, int lane,
+                                             float scale_log2) {
+  using S = DecodeShape<D>;
+  const int n16 = lane & 15;
+  const int q4 = lane >> 4;
+
+  f32x4 s[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    s[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < S::KK; ++kk) s[hf] = mfma16x16x32(r.k[hf][kk], qb[kk], s[hf]);
+  }
+
+  // Online softmax in the log2 domain; lane owns head n16 for tokens
+  // 16*hf + 4*q4 + i of the tile.
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[hf][i] *= scale_log2;
+  if (j0 + kDecTile > t1) {  // partial tile: mask the tokens past the context
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j0 + hf * 16 + 4 * q4 + i >= t1) s[hf][i] = -INFINITY;
+  }
+  float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mt = wave_max_xor_16_32(mt);
+  const float m_new = fmaxf(m, mt);
+  float p[2][4];
+  float ps = 0.f;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[hf][i] = fast_exp2(s[hf][i] - m_new);
+      ps += p[hf][i];
+    }
+  if (__ballot(m_new > m) != 0) {  // rescale only when some running max grew
+    const float alpha = fast_exp2(m - m_new);
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < S::DB; ++c) o[c] *= alpha;
+    m = m_new;
+  }
+  lsum += ps;
+  const u32x4 pb = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                    pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+
+  // Stage V row-major, then read V^T operands with the transposing LDS load:
+  // k-slot t of lane quarter q4 is token 16*(t/4) + 4*q4 + t%4, the token
+  // order of the probabilities above.
+  wave_lds_sync();
+  {
+    const int piece = lane % S::CH;
+    const int row0 = lane / S::CH;
+#pragma unroll
+    for (int e = 0; e < S::VLOADS; ++e)
+      *(lds_u32x4*)(vst + (e * S::ROWS_PER_LOAD + row0) * S::VROW + 16 * piece) = r.v[e];
+  }
+  wave_lds_sync();
+  const lds_bytes rd = vst + (4 * q4 + (n16 >> 2)) * S::VROW + 8 * (n16 & 3);
+#pragma unroll
+  for (int c = 0; c < S::DB; ++c) {
+    const uint2 lo = lds_read_tr16(rd + 32 * c);
+    const uint2 hi = lds_read_tr16(rd + 16 * S::VROW + 32 * c);
+    o[c] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, o[c]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / a.head_groups;
-  const int hg = blockIdx.y - g * a.head_groups;
-  const int b = blockIdx.z;
+  // Work item order: split index slowest, then sequence, then kv head.
+  // Workgroups are dispatched round-robin over the 8 XCDs, so with 8 | Hkv
+  // every XCD serves whole kv heads of every sequence (an even share of long
+  // and short contexts), and the first splits of all sequences start first.
+  const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.head_groups;
+  const int64_t lin = blockIdx.x;
+  const int split = static_cast<int>(lin / pairs);
+  const int64_t pair = lin - split * pairs;
+  const int gy = static_cast<int>(pair % (a.num_kv_heads * a.head_groups));
+  const int b = static_cast<int>(pair / (a.num_kv_heads * a.head_groups));
+  const int g = gy / a.head_groups;
+  const int hg = gy - g * a.head_groups;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
 
@@ -98,100 +252,41 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
   float m = -INFINITY;
   float lsum = 0.f;
 
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+  gtable bt = (gtable)(a.block_tables) + static_cast<int64_t>(b) * a.max_blocks_per_seq;
   const int shift = a.block_shift;
-  const int bmask = (1 << shift) - 1;
   const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * D;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + static_cast<int64_t>(g) * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + static_cast<int64_t>(g) * D;
-  unsigned char* vst = smem + wave * kDecTile * S::VROW;
-  const int vpiece = lane % S::CH;
-  const int vrow0 = lane / S::CH;
+  const uint32_t row_bytes = static_cast<uint32_t>(row_elems * 2);
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  lds_bytes vst = (lds_bytes)smem + wave * kDecTile * S::VROW;
+  // Per-lane byte offsets inside a half: K lane (n16, q4) reads token n16,
+  // head-dim values 8*q4 + 32*kk; V lane reads 16-byte piece lane % CH of row
+  // lane / CH (+ ROWS_PER_LOAD per load).
+  const uint32_t koff = n16 * row_bytes + 16 * q4;
+  uint32_t voff[S::VLOADS];
+#pragma unroll
+  for (int e = 0; e < S::VLOADS; ++e)
+    voff[e] = ((e * S::ROWS_PER_LOAD + lane / S::CH) & 15) * row_bytes + 16 * (lane % S::CH);
 
-  for (int j0 = t0 + wave * kDecTile; j0 < t1; j0 += kDecWaves * kDecTile) {
-    // Slots of the two 16-token halves; a half never crosses a block boundary
-    // because block_size >= 16 and j0 is a multiple of 16.
-    const int64_t slot0 = (static_cast<int64_t>(bt[j0 >> shift]) << shift) + (j0 & bmask);
-    const int j1 = j0 + 16;
-    const int64_t slot1 =
-        (j1 < t1) ? (static_cast<int64_t>(bt[j1 >> shift]) << shift) + (j1 & bmask) : slot0;
-
-    u32x4 ka[2][S::KK];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const bool live = j0 + hf * 16 + n16 < t1;
-      const uint16_t* kp = kbase + ((hf ? slot1 : slot0) + n16) * row_elems + 8 * q4;
-#pragma unroll
-      for (int kk = 0; kk < S::KK; ++kk) ka[hf][kk] = live ? ldg16(kp + 32 * kk) : u32x4{0, 0, 0, 0};
-    }
-    u32x4 vr[S::VREGS];
-#pragma unroll
-    for (int e = 0; e < S::VREGS; ++e) {
-      const int row = e * S::ROWS_PER_LOAD + vrow0;
-      const bool live = j0 + row < t1;
-      const uint16_t* vp = vbase + ((row < 16 ? slot0 : slot1) + (row & 15)) * row_elems + 8 * vpiece;
-      vr[e] = live ? ldg16(vp) : u32x4{0, 0, 0, 0};
-    }
-
-    f32x4 s[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      s[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < S::KK; ++kk) s[hf] = mfma16x16x32(ka[hf][kk], qb[kk], s[hf]);
-    }
-
-    // Online softmax in the log2 domain; lane owns head n16 for tokens 4*q4+i.
-    float mt = -INFINITY;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool live = j0 + hf * 16 + 4 * q4 + i < t1;
-        const float x = live ? s[hf][i] * a.scale_log2 : -INFINITY;
-        s[hf][i] = x;
-        mt = fmaxf(mt, x);
-      }
-    }
-    mt = wave_max_xor_16_32(mt);
-    const float m_new = fmaxf(m, mt);
-    const float alpha = fast_exp2(m - m_new);
-    float p[2][4];
-    float ps = 0.f;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[hf][i] = fast_exp2(s[hf][i] - m_new);
-        ps += p[hf][i];
-      }
-    }
-    lsum = lsum * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int c = 0; c < S::DB; ++c) o[c] *= alpha;
-    const u32x4 pb = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                      pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-
-    // Stage the V tile (row-major) and read V^T operands column-wise.
-    wave_lds_sync();
-#pragma unroll
-    for (int e = 0; e < S::VREGS; ++e) {
-      const int row = e * S::ROWS_PER_LOAD + vrow0;
-      *reinterpret_cast<u32x4*>(vst + row * S::VROW + 16 * vpiece) = vr[e];
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int c = 0; c < S::DB; ++c) {
-      const unsigned char* col = vst + (16 * c + n16) * 2;
-      uint32_t w[4];
-#pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        const uint32_t lo = *reinterpret_cast<const uint16_t*>(col + tile_token(q4, t) * S::VROW);
-        const uint32_t hi = *reinterpret_cast<const uint16_t*>(col + tile_token(q4, t + 1) * S::VROW);
-        w[t / 2] = lo | (hi << 16);
-      }
-      o[c] = mfma16x16x32(u32x4{w[0], w[1], w[2], w[3]}, pb, o[c]);
+  // Software pipeline over this wave's tiles (wave, wave + 4, ...): the loads
+  // of tile i + 1 are in flight while tile i is computed.
+  constexpr int kStride = kDecWaves * kDecTile;
+  const int j_first = t0 + wave * kDecTile;
+  const int n_tiles = j_first < t1 ? (t1 - j_first + kStride - 1) / kStride : 0;
+  if (n_tiles > 0) {
+    TileRegs<D> ra, rb;
+    load_tile<D>(ra, kc, vc, bt, j_first, t1, t0, shift, row_elems, g, koff, voff);
+    // (the scheduling barriers keep the compiler from hoisting the current
+    // tile's math, and with it a wait for the loads, above the next loads)
+    for (int it = 0; it < n_tiles; it += 2) {
+      const int j = j_first + it * kStride;
+      load_tile<D>(rb, kc, vc, bt, j + kStride, t1, t0, shift, row_elems, g, koff, voff);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile<D>(ra, qb, o, m, lsum, vst, j, t1, lane, a.scale_log2);
+      if (it + 1 >= n_tiles) break;
+      load_tile<D>(ra, kc, vc, bt, j + 2 * kStride, t1, t0, shift, row_elems, g, koff, voff);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile<D>(rb, qb, o, m, lsum, vst, j + kStride, t1, lane, a.scale_log2);
     }
   }
 
@@ -228,7 +323,7 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
       }
     }
     if (a.n_split == 1) {
-      out[idx] = static_cast<uint16_t>(bf16_rne(L > 0.f ? O / L : 0.f));
+      out[idx] = bf16_bits(L > 0.f ? O / L : 0.f);
     } else {
       const int64_t pidx = (static_cast<int64_t>(b) * a.num_q_heads + h0 + hl) * a.n_split + split;
       a.part_o[pidx * D + d] = O;
@@ -244,8 +339,8 @@ __global__ __launch_bounds__(kDecThreads) void paged_decode_kernel(DecodeArgs a)
 // sum_s 2^(m_s - M) l_s, M = max_s m_s (scores are in the log2 domain).
 template <int D>
 __global__ __launch_bounds__(D) void paged_decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  const int h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.num_q_heads));
+  const int b = static_cast<int>(blockIdx.x / static_cast<uint32_t>(a.num_q_heads));
   const int d = threadIdx.x;
   const int ctx = a.context_lens[b];
   const int n = min(a.n_split, (ctx + a.split_tokens - 1) / a.split_tokens);
@@ -260,7 +355,7 @@ __global__ __launch_bounds__(D) void paged_decode_combine_kernel(DecodeArgs a) {
   }
   uint16_t* out = static_cast<uint16_t*>(a.out);
   out[(static_cast<int64_t>(b) * a.num_q_heads + h) * D + d] =
-      static_cast<uint16_t>(bf16_rne((n > 0 && L > 0.f) ? O / L : 0.f));
+      bf16_bits((n > 0 && L > 0.f) ? O / L : 0.f);
 }
 
 }  // namespace
@@ -269,20 +364,24 @@ int32_t decode_auto_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_hea
                           int32_t max_context_len) {
   const int32_t group = num_q_heads / num_kv_heads;
   const int64_t pairs = static_cast<int64_t>(batch) * num_kv_heads * ((group + 15) / 16);
-  // Aim for a few thousand workgroups so the 256 CUs stay busy to the end;
-  // never split below 256 tokens and never let one workgroup walk more than 2048.
-  const int64_t want = 4096;
-  int64_t n = pairs > 0 ? (want + pairs - 1) / pairs : 1;
+  // Aim for at least ~2048 workgroups (eight per CU) so the tail is short;
+  // never split below 256 tokens and never let one workgroup walk more than
+  // kMaxSplit tokens (long contexts then spread over many CUs).
+  constexpr int64_t kWantWGs = 2048;
+  constexpr int64_t kMaxSplit = 4096;
+  int64_t n = pairs > 0 ? (kWantWGs + pairs - 1) / pairs : 1;
   if (n < 1) n = 1;
   int64_t split = (static_cast<int64_t>(max_context_len) + n - 1) / n;
-  split = (split + 127) / 128 * 128;
+  split = (split + 255) / 256 * 256;
   if (split < 256) split = 256;
-  if (split > 2048) split = 2048;
+  if (split > kMaxSplit) split = kMaxSplit;
   return static_cast<int32_t>(split);
 }
 
-hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.n_split, a.num_kv_heads * a.head_groups, a.batch);
+hipError_t launch_paged_decode(const DecodeArgs& args, hipStream_t stream) {
+  const DecodeArgs& a = args;
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.n_split) * a.num_kv_heads *
+                                        a.head_groups * a.batch));
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(paged_decode_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
   } else {
@@ -290,7 +389,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.n_split == 1) return err;
-  const dim3 cgrid(a.num_q_heads, a.batch);
+  const dim3 cgrid(static_cast<uint32_t>(a.num_q_heads) * static_cast<uint32_t>(a.batch));
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(paged_decode_combine_kernel<128>, cgrid, dim3(128), 0, stream, a);
   } else {

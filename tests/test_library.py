@@ -84,7 +84,12 @@ def test_decode_plan(lib):
         pkv.decode_workspace_bytes(4, 6, 4, 64, 100)
     for args in [(256, 16, 8, 128, 1024), (512, 64, 8, 128, 32768), (4, 8, 2, 64, 700)]:
         split = pkv.decode_split_tokens(*args)
-        assert split >= 256 and split % 128 == 0 and split <= 2048
+        assert 256 <= split <= 4096 and split % 256 == 0
+    # whole sequences when there are enough (sequence, kv head) pairs to fill the chip
+    assert pkv.decode_split_tokens(256, 16, 8, 128, 1024) == 1024
+    # long contexts are cut into bounded pieces; tiny batches into single blocks
+    assert pkv.decode_split_tokens(512, 64, 8, 128, 32768) == 4096
+    assert pkv.decode_split_tokens(4, 8, 2, 64, 700) == 256
 
 
 def _prefill(lib, ns=2, tq=10, mq=5, mk=5, hq=4, hkv=2, d=64, bs=16, mb=1, causal=1, out=16):
