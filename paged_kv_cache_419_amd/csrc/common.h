@@ -24,6 +24,65 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D = C + A * B on one 32x32x16 bf16 MFMA tile (fp32 accumulate).
+// Lane l supplies A[l % 32][8 * (l / 32) + t] and B[8 * (l / 32) + t][l % 32]
+// for t = 0..7, and receives C[8 * j + 4 * (l / 32) + i][l % 32] in element
+// 4 * j + i (j, i = 0..3).
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// LDS pointers with the address space spelled out, so the compiler knows
+// stores through them cannot touch global memory.
+typedef __attribute__((address_space(3))) unsigned char* lds_bytes;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group,
+// lane i addresses 4 consecutive 16-bit values that form row i / 4, columns
+// 4 * (i % 4) .. +3 of a 4 x 16 block; lane j of the group receives column j
+// (rows 0..3).
+__device__ __forceinline__ uint2 lds_read_tr16(lds_bytes p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
+}
+
+// Direct-to-LDS load (gfx950 global_load_lds_dwordx4): every lane reads 16
+// bytes at its own global address `src`; lane i's bytes land at LDS byte
+// address `dst` + 16 * i (`dst` must be the same for the whole wave).  Issued
+// from inline asm so that the compiler inserts no waits of its own for these
+// loads; callers wait with barrier_after_loads.  M0 is saved and restored.
+__device__ __forceinline__ void lds_dma16(const void* src, lds_bytes dst) {
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
+// Workgroup barrier once at most N vector-memory loads of this wave are still
+// outstanding (direct-to-LDS loads included): this wave's older loads have
+// landed, younger ones stay in flight.  One asm statement with a memory
+// clobber, so the compiler moves no memory access across it.
+template <int N>
+__device__ __forceinline__ void barrier_after_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier once this wave's LDS accesses have completed.
+__device__ __forceinline__ void barrier_after_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> packed pair of bf16 (lo in bits 0..15), round to nearest even

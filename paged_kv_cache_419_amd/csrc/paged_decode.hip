@@ -68,10 +68,7 @@ struct TileRegs {
 // Block-table entries are read with scalar loads: the index is the same for
 // the whole wave and the table is never written by the kernel.
 typedef const __attribute__((address_space(4))) int32_t* gtable;
-// LDS pointers with their address space spelled out, so the compiler knows
-// the staging stores cannot touch global memory.
-typedef __attribute__((address_space(3))) unsigned char* lds_bytes;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
 
 // Buffer descriptor of the 16 token rows of one kv head starting at logical
 // position j (a multiple of 16) of a sequence; `live` of them are readable
@@ -115,14 +112,6 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* kc, co
     const bool second = e * S::ROWS_PER_LOAD >= 16;
     r.v[e] = buffer_load16(second ? v1 : v0, voff[e]);
   }
-}
-
-// Transposed LDS read: lane (n16, q4) of the result holds column n16 of the
-// 4 x 16 block whose rows its 16-lane group addresses (ds_read_b64_tr_b16).
-__device__ __forceinline__ uint2 lds_read_tr16(lds_bytes p) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p));
 }
 
 template <int D>

@@ -11,18 +11,26 @@
 // Work split.  A workgroup (4 waves) owns one (sequence, kv head, q tile).  Its
 // waves cover up to four query heads of that kv head and 32 query rows each
 // (4 heads x 32 rows at GQA ratio 4, 2 x 64 at ratio 2, 1 x 128 without GQA),
-// so one K/V tile in LDS serves 128 (row, head) pairs.  Workgroup ids are
-// remapped so that consecutive q tiles of one (sequence, kv head) run on the
-// same XCD and share its L2.
+// so one K/V tile in LDS serves 128 (row, head) pairs.  Work items are ordered
+// q tile (latest first: those rows see the most keys), then sequence, then kv
+// head; workgroups go round-robin to the 8 XCDs, so with 8 | Hkv every XCD
+// serves one kv head and keeps that head's K/V (a shared prefix especially)
+// in its own L2.
 //
-// Per 64-key tile the workgroup copies K (row-major) and V (transposed, with
-// the key order the MFMA k-slots use) into LDS; then each wave computes
-// S^T[key][row] = K Q^T on 16x16x32 bf16 MFMAs (Q^T held in registers),
-// applies the causal mask and an online softmax per query row (each lane owns
-// one row of each 16-row block, so rescaling is lane-local and the
-// probabilities already sit in the B-operand layout of the next product), and
-// accumulates O^T[d][row] += V^T P^T on the same MFMA shape.  fp32 accumulation;
-// probabilities are rounded to bf16 for the second product.
+// Pipeline.  K and V tiles of 64 keys go straight from HBM into LDS with the
+// gfx950 direct-to-LDS loads (global_load_lds_dwordx4), double-buffered: the
+// next tile's loads are in flight while the current tile is computed.  Rows
+// are stored with XOR-swizzled 16-byte chunks so that both the K operand reads
+// and the transposing V reads are free of bank conflicts.  Key rows past Lk
+// are redirected to key Lk - 1 (a live row), so stale or poisoned slots are
+// never read; their scores are masked.
+//
+// Matrix cores.  Each wave computes S^T[key][row] = K Q^T on 32x32x16 bf16
+// MFMAs with Q^T held in registers.  In that output layout a lane holds 32
+// scores of one query row, so the online softmax needs a single cross-lane
+// exchange per tile, and the probabilities already sit in the B-operand layout
+// of O^T[d][row] += V^T P^T, whose V^T operand comes from ds_read_b64_tr_b16.
+// fp32 accumulation; probabilities are rounded to bf16 for the second product.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,221 +40,289 @@ namespace {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfKeys = 64;  // keys per LDS tile
-constexpr int kPfRows = 32;  // query rows per wave: two 16-row MFMA blocks
+constexpr int kPfKeys = 64;  // keys per tile
+constexpr int kPfRows = 32;  // query rows per wave (the N side of a 32x32 MFMA)
 
 template <int D>
 struct PrefillShape {
-  static constexpr int KK = D / 32;
-  static constexpr int DB = D / 16;
-  static constexpr int CH = D / 8;
-  static constexpr int KROW = D * 2 + 16;          // LDS bytes per K row (padded)
-  static constexpr int VTROW = kPfKeys * 2 + 16;   // LDS bytes per V^T row (one d)
-  static constexpr int KLOADS = kPfKeys * CH / kPfThreads;
-  static constexpr int LDS = kPfKeys * KROW + D * VTROW;
+  static constexpr int KS = D / 16;                 // k-steps of S^T = K Q^T
+  static constexpr int DC = D / 32;                 // 32-row blocks of O^T
+  static constexpr int CH = D / 8;                  // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;                // LDS bytes per key row
+  static constexpr int TILE = kPfKeys * ROWB;       // one K (or V) tile
+  static constexpr int RPL = kWave / CH;            // rows per wave-wide direct load
+  static constexpr int LOADS = kPfKeys / kPfWaves / RPL;  // per wave, per tensor, per tile
 };
+
+// Chunk position of 16-byte chunk c of key row r in LDS (an involution in c).
+// K: 16 consecutive rows read at one chunk hit 16 distinct bank groups.
+// V: 4 consecutive rows x 4 consecutive chunks (one transposing read) hit 16.
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+struct SeqView {
+  const uint16_t* kc;  // k_cache + g * D (elements)
+  const uint16_t* vc;
+  const __attribute__((address_space(4))) int32_t* bt;
+  int lk;
+  int shift;
+  uint32_t row_bytes;
+};
+
+// Issue this wave's share of the K and V tile starting at key k0 into LDS
+// (rows 16 * wave .. 16 * wave + 15 of each tile).
+template <int D>
+__device__ __forceinline__ void issue_tile(const SeqView& sv, int k0, int wave, int lane,
+                                           lds_bytes kdst, lds_bytes vdst) {
+  using S = PrefillShape<D>;
+  const int bmask = (1 << sv.shift) - 1;
+  // The wave's 16 rows lie in one cache block (blocks hold >= 16 tokens and
+  // the rows start at a multiple of 16); rows past Lk are redirected to key
+  // Lk - 1, which then lies in that same block or is the only key loaded.
+  const int kfirst = min(k0 + wave * (kPfKeys / kPfWaves), sv.lk - 1);
+  const int64_t blk = sv.bt[kfirst >> sv.shift];
+  const int64_t base = (blk << sv.shift) * static_cast<int64_t>(sv.row_bytes);
+#pragma unroll
+  for (int e = 0; e < S::LOADS; ++e) {
+    const int rr0 = wave * (kPfKeys / kPfWaves) + e * S::RPL;  // first row of this load
+    const int rr = rr0 + lane / S::CH;
+    const int p = lane % S::CH;
+    const int kcl = min(k0 + rr, sv.lk - 1);
+    const uint32_t roff = static_cast<uint32_t>(kcl & bmask) * sv.row_bytes;
+    const char* ksrc = reinterpret_cast<const char*>(sv.kc) + base + roff + 16 * (p ^ kswz<D>(rr));
+    const char* vsrc = reinterpret_cast<const char*>(sv.vc) + base + roff + 16 * (p ^ vswz<D>(rr));
+    lds_dma16(ksrc, kdst + rr0 * S::ROWB);
+    lds_dma16(vsrc, vdst + rr0 * S::ROWB);
+  }
+}
+
+template <int D>
+struct WaveState {
+  u32x4 qb[PrefillShape<D>::KS];      // B operand Q^T per k-step
+  f32x16 o[PrefillShape<D>::DC];      // O^T accumulators
+  float m;                            // running max (log2 domain) of this lane's row
+  float l;                            // running sum over this lane's half of the keys
+};
+
+// One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_bytes vt,
+                                             const uint32_t (&kaddr)[PrefillShape<D>::KS],
+                                             const uint32_t (&vaddr)[PrefillShape<D>::DC],
+                                             int k0, int lim, bool need_mask, int h,
+                                             float c) {
+  using S = PrefillShape<D>;
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      const u32x4 a = *(const lds_u32x4*)(kt + kaddr[ks] + kb * 32 * S::ROWB);
+      s[kb] = mfma32x32x16(a, w.qb[ks], s[kb]);
+    }
+  }
+  // element 4j + i of s[kb] is key k0 + 32 kb + 8 j + 4 h + i of this lane's row
+  if (need_mask) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (k0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3) > lim) s[kb][v] = -INFINITY;
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(w.m, mx * c);
+  if (__ballot(m_new > w.m) != 0) {  // rescale only when some running max grew
+    const float alpha = fast_exp2(w.m - m_new);
+    w.l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < S::DC; ++cb) w.o[cb] *= alpha;
+    w.m = m_new;
+  }
+  u32x4 pb[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = fast_exp2(__builtin_fmaf(s[kb][v], c, -w.m));
+      w.l += p[v];
+    }
+    // 16-key block u = 2 kb + hb: k-slots 0..3 are keys 16u + 4h + i,
+    // k-slots 4..7 are keys 16u + 8 + 4h + i
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int j = 2 * hb;
+      pb[2 * kb + hb] = u32x4{pack_bf16x2(p[4 * j], p[4 * j + 1]), pack_bf16x2(p[4 * j + 2], p[4 * j + 3]),
+                              pack_bf16x2(p[4 * j + 4], p[4 * j + 5]),
+                              pack_bf16x2(p[4 * j + 6], p[4 * j + 7])};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int cb = 0; cb < S::DC; ++cb) {
+      const uint2 lo = lds_read_tr16(vt + vaddr[cb] + 16 * u * S::ROWB);
+      const uint2 hi = lds_read_tr16(vt + vaddr[cb] + (16 * u + 8) * S::ROWB);
+      w.o[cb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[u], w.o[cb]);
+    }
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
     PrefillArgs a, int32_t heads_per_wg, int32_t head_groups, int32_t rows_per_wg,
-    int32_t q_tiles, int64_t total_items, int64_t items_per_xcd) {
+    int32_t q_tiles) {
   using S = PrefillShape<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS];
-  unsigned char* ks = smem;
-  unsigned char* vts = smem + kPfKeys * S::KROW;
+  __shared__ __attribute__((aligned(1024))) unsigned char buf_a[2 * S::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char buf_b[2 * S::TILE];
 
-  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous range of work items.
-  const int64_t lin = blockIdx.x;
-  const int64_t item = (lin % 8) * items_per_xcd + lin / 8;
-  if (item >= total_items) return;
-  int64_t rest = item;
-  const int qt = static_cast<int>(rest % q_tiles);
-  rest /= q_tiles;
+  // item = ((q tile rank * num_seqs + seq) * Hkv + g) * head_groups + hg
+  int64_t rest = blockIdx.x;
   const int hg = static_cast<int>(rest % head_groups);
   rest /= head_groups;
   const int g = static_cast<int>(rest % a.num_kv_heads);
-  const int seq = static_cast<int>(rest / a.num_kv_heads);
+  rest /= a.num_kv_heads;
+  const int seq = static_cast<int>(rest % a.num_seqs);
+  const int qtile = q_tiles - 1 - static_cast<int>(rest / a.num_seqs);
 
   const int q_start = a.cu_q[seq];
   const int lq = a.cu_q[seq + 1] - q_start;
   const int lk = a.cu_k[seq + 1] - a.cu_k[seq];
   const int off = lk - lq;
-  const int qtile = q_tiles - 1 - qt;  // longer causal rows first within a sequence
   const int r0 = qtile * rows_per_wg;
   if (r0 >= lq) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int n16 = lane & 15;
-  const int q4 = lane >> 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int m32 = lane & 31;
+  const int h = lane >> 5;
   const int hl = hg * heads_per_wg + wave % heads_per_wg;
   const bool hvalid = hl < a.group;
-  const int h = g * a.group + (hvalid ? hl : 0);
+  const int head = g * a.group + (hvalid ? hl : 0);
   const int rbase = r0 + (wave / heads_per_wg) * kPfRows;
+  const int row = rbase + m32;
 
-  // B operands of S^T = K Q^T: lane holds 8 values of query row n16 per block.
-  u32x4 qb[2][S::KK];
-  int lim[2];  // last visible key position of this lane's row in each block
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = rbase + rb * 16 + n16;
-    const bool live = hvalid && r < lq;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<int64_t>(q_start + r) * a.num_q_heads + h) * D + 8 * q4;
-#pragma unroll
-    for (int kk = 0; kk < S::KK; ++kk) qb[rb][kk] = live ? ldg16(qp + 32 * kk) : u32x4{0, 0, 0, 0};
-    const int rc = min(r, lq - 1);  // padding rows borrow the last row's mask
-    lim[rb] = a.causal ? min(off + rc, lk - 1) : lk - 1;
-  }
+  SeqView sv;
+  sv.row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+  sv.kc = static_cast<const uint16_t*>(a.k_cache) + static_cast<int64_t>(g) * D;
+  sv.vc = static_cast<const uint16_t*>(a.v_cache) + static_cast<int64_t>(g) * D;
+  sv.bt = (const __attribute__((address_space(4))) int32_t*)(a.block_tables) +
+          static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+  sv.lk = lk;
+  sv.shift = a.block_shift;
+  lds_bytes ka = (lds_bytes)buf_a;
+  lds_bytes va = (lds_bytes)buf_a + S::TILE;
+  lds_bytes kb_ = (lds_bytes)buf_b;
+  lds_bytes vb = (lds_bytes)buf_b + S::TILE;
+
   const int last_row = min(r0 + rows_per_wg, lq) - 1;
   const int kend = a.causal ? min(lk, off + last_row + 1) : lk;
+  const int n_tiles = (kend + kPfKeys - 1) / kPfKeys;
+  if (n_tiles > 0) issue_tile<D>(sv, 0, wave, lane, ka, va);
 
-  f32x4 o[2][S::DB];
+  WaveState<D> w;
+  // With a negative scale, negate Q (exact in bf16) and use |scale|, so the
+  // exponent scale c is positive and the row max of raw scores is the max.
+  const float c = fabsf(a.scale_log2);
+  {
+    const bool live = hvalid && row < lq;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<int64_t>(q_start + (live ? row : 0)) * a.num_q_heads + head) * D +
+                         8 * h;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int ks = 0; ks < S::KS; ++ks) w.qb[ks] = live ? ldg16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+    // Q (and tile 0) must have landed before the loop: a wait the compiler
+    // sees, so it adds none inside the loop, where the only vector loads are
+    // the direct-to-LDS ones it does not track.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (a.scale_log2 < 0.f) {
 #pragma unroll
-    for (int c = 0; c < S::DB; ++c) o[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
-
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
-  const int shift = a.block_shift;
-  const int bmask = (1 << shift) - 1;
-  const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * D;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + static_cast<int64_t>(g) * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + static_cast<int64_t>(g) * D;
-
-  for (int k0 = 0; k0 < kend; k0 += kPfKeys) {
-    __syncthreads();  // the previous tile is consumed
-    // K tile, row-major: one 16-byte piece per thread per load.
-#pragma unroll
-    for (int e = 0; e < S::KLOADS; ++e) {
-      const int row = e * (kPfThreads / S::CH) + tid / S::CH;
-      const int piece = tid % S::CH;
-      const int key = k0 + row;
-      u32x4 val = {0, 0, 0, 0};
-      if (key < lk) {
-        const int64_t slot = (static_cast<int64_t>(bt[key >> shift]) << shift) + (key & bmask);
-        val = ldg16(kbase + slot * row_elems + 8 * piece);
-      }
-      *reinterpret_cast<u32x4*>(ks + row * S::KROW + 16 * piece) = val;
+      for (int ks = 0; ks < S::KS; ++ks) w.qb[ks] ^= 0x80008000u;
     }
-    // V tile, transposed: a thread takes 4 consecutive keys x 8 values of d and
-    // writes, for each d, the 4 keys as one 8-byte run of V^T row d.  Key k of
-    // the tile goes to position 32*(k/32) + 8*((k%16)/4) + 4*((k%32)/16) + k%4,
-    // the order in which the PV MFMA k-slots expect it.
-    if (tid < 16 * S::CH) {
-      const int quad = tid / S::CH;
-      const int piece = tid % S::CH;
-      u32x4 vk[4];
+  }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = k0 + 4 * quad + e;
-        vk[e] = u32x4{0, 0, 0, 0};
-        if (key < lk) {
-          const int64_t slot = (static_cast<int64_t>(bt[key >> shift]) << shift) + (key & bmask);
-          vk[e] = ldg16(vbase + slot * row_elems + 8 * piece);
-        }
-      }
-      const int pos = (quad / 8) * 32 + 8 * (quad % 4) + 4 * ((quad / 4) % 2);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d = 8 * piece + 2 * w;
-        const uint32_t lo0 = (vk[0][w] & 0xFFFFu) | (vk[1][w] << 16);
-        const uint32_t lo1 = (vk[2][w] & 0xFFFFu) | (vk[3][w] << 16);
-        const uint32_t hi0 = (vk[0][w] >> 16) | (vk[1][w] & 0xFFFF0000u);
-        const uint32_t hi1 = (vk[2][w] >> 16) | (vk[3][w] & 0xFFFF0000u);
-        *reinterpret_cast<uint2*>(vts + d * S::VTROW + 2 * pos) = uint2{lo0, lo1};
-        *reinterpret_cast<uint2*>(vts + (d + 1) * S::VTROW + 2 * pos) = uint2{hi0, hi1};
-      }
-    }
-    __syncthreads();
-    if (!hvalid) continue;
+  for (int cb = 0; cb < S::DC; ++cb) w.o[cb] = f32x16{};
+  w.m = -INFINITY;
+  w.l = 0.f;
 
-    // S^T[key][row] for 4 key blocks x 2 row blocks.
-    f32x4 s[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < S::KK; ++kk) {
-        const u32x4 ka =
-            *reinterpret_cast<const u32x4*>(ks + (kb * 16 + n16) * S::KROW + 2 * (32 * kk + 8 * q4));
-        s[kb][0] = mfma16x16x32(ka, qb[0][kk], s[kb][0]);
-        s[kb][1] = mfma16x16x32(ka, qb[1][kk], s[kb][1]);
-      }
-    }
+  // last visible key of this lane's row (padding rows borrow the last row's)
+  const int lim = a.causal ? min(off + min(row, lq - 1), lk - 1) : lk - 1;
+  // smallest such limit over this wave's rows, and the wave's largest
+  const int lim_lo = a.causal ? min(off + min(rbase, lq - 1), lk - 1) : lk - 1;
+  const int lim_hi = a.causal ? min(off + min(rbase + kPfRows - 1, lq - 1), lk - 1) : lk - 1;
 
-    u32x4 pb[2][2];
+  // Per-lane LDS byte offsets of the MFMA operands inside a tile.
+  uint32_t kaddr[S::KS];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float mt = -INFINITY;
+  for (int ks = 0; ks < S::KS; ++ks)
+    kaddr[ks] = m32 * S::ROWB + 16 * ((2 * ks + h) ^ kswz<D>(m32));
+  uint32_t vaddr[S::DC];
+  {
+    const int gi = lane & 15;        // lane inside its 16-lane group
+    const int dsub = (lane >> 4) & 1;
+    const int vr = 4 * h + (gi >> 2);  // key row (mod 16) this lane addresses
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + kb * 16 + 4 * q4 + i;
-          const float x = key <= lim[rb] ? s[kb][rb][i] * a.scale_log2 : -INFINITY;
-          s[kb][rb][i] = x;
-          mt = fmaxf(mt, x);
-        }
-      }
-      mt = wave_max_xor_16_32(mt);
-      const float m_new = fmaxf(m[rb], mt);
-      const float alpha = fast_exp2(m[rb] - m_new);
-      float ps = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = fast_exp2(s[kb][rb][i] - m_new);
-          ps += p[kb][i];
-        }
-      }
-      l[rb] = l[rb] * alpha + ps;
-      m[rb] = m_new;
-#pragma unroll
-      for (int c = 0; c < S::DB; ++c) o[rb][c] *= alpha;
-#pragma unroll
-      for (int g32 = 0; g32 < 2; ++g32) {
-        pb[rb][g32] = u32x4{pack_bf16x2(p[2 * g32][0], p[2 * g32][1]),
-                            pack_bf16x2(p[2 * g32][2], p[2 * g32][3]),
-                            pack_bf16x2(p[2 * g32 + 1][0], p[2 * g32 + 1][1]),
-                            pack_bf16x2(p[2 * g32 + 1][2], p[2 * g32 + 1][3])};
-      }
-    }
-
-    // O^T[d][row] += V^T P^T.
-#pragma unroll
-    for (int c = 0; c < S::DB; ++c) {
-#pragma unroll
-      for (int g32 = 0; g32 < 2; ++g32) {
-        const u32x4 va =
-            *reinterpret_cast<const u32x4*>(vts + (16 * c + n16) * S::VTROW + 2 * (32 * g32 + 8 * q4));
-        o[0][c] = mfma16x16x32(va, pb[0][g32], o[0][c]);
-        o[1][c] = mfma16x16x32(va, pb[1][g32], o[1][c]);
-      }
+    for (int cb = 0; cb < S::DC; ++cb) {
+      const int chunk = 4 * cb + 2 * dsub + ((gi & 3) >> 1);
+      vaddr[cb] = vr * S::ROWB + 16 * (chunk ^ vswz<D>(vr)) + 8 * (gi & 1);
     }
   }
 
-  if (!hvalid) return;
+  // Double-buffered tile loop (unrolled by two so each LDS buffer is a
+  // distinct array and the compiler never waits on the other buffer's loads).
+  // Before the first barrier of a tile each wave waits for its own loads of
+  // that tile (the next tile's stay in flight); the second barrier keeps the
+  // buffer from being refilled while another wave still reads it.
+  constexpr int kInFlight = 2 * S::LOADS;
+  for (int t = 0; t < n_tiles; t += 2) {
+    if (t + 1 < n_tiles) {
+      issue_tile<D>(sv, (t + 1) * kPfKeys, wave, lane, kb_, vb);
+      barrier_after_loads<kInFlight>();
+    } else {
+      barrier_after_loads<0>();
+    }
+    {
+      const int k0 = t * kPfKeys;
+      if (hvalid && k0 <= lim_hi)
+        compute_tile<D>(w, ka, va, kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
+    }
+    barrier_after_lds();
+    if (t + 1 >= n_tiles) break;
+    if (t + 2 < n_tiles) {
+      issue_tile<D>(sv, (t + 2) * kPfKeys, wave, lane, ka, va);
+      barrier_after_loads<kInFlight>();
+    } else {
+      barrier_after_loads<0>();
+    }
+    {
+      const int k0 = (t + 1) * kPfKeys;
+      if (hvalid && k0 <= lim_hi)
+        compute_tile<D>(w, kb_, vb, kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
+    }
+    barrier_after_lds();
+  }
+
+  if (!hvalid || row >= lq) return;
+  const float lt = w.l + __shfl_xor(w.l, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  uint16_t* op = static_cast<uint16_t*>(a.out) +
+                 (static_cast<int64_t>(q_start + row) * a.num_q_heads + head) * D + 4 * h;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float lt = wave_sum_xor_16_32(l[rb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int r = rbase + rb * 16 + n16;
-    if (r >= lq) continue;
-    uint16_t* op = static_cast<uint16_t*>(a.out) +
-                   (static_cast<int64_t>(q_start + r) * a.num_q_heads + h) * D + 4 * q4;
+  for (int cb = 0; cb < S::DC; ++cb) {
 #pragma unroll
-    for (int c = 0; c < S::DB; ++c) {
-      const uint2 w = {pack_bf16x2(o[rb][c][0] * inv, o[rb][c][1] * inv),
-                       pack_bf16x2(o[rb][c][2] * inv, o[rb][c][3] * inv)};
-      *reinterpret_cast<uint2*>(op + 16 * c) = w;
+    for (int j = 0; j < 4; ++j) {
+      const f32x16& ov = w.o[cb];
+      const uint2 v = {pack_bf16x2(ov[4 * j] * inv, ov[4 * j + 1] * inv),
+                       pack_bf16x2(ov[4 * j + 2] * inv, ov[4 * j + 3] * inv)};
+      *reinterpret_cast<uint2*>(op + 32 * cb + 8 * j) = v;
     }
   }
 }
@@ -261,14 +337,13 @@ hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int64_t total =
       static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * head_groups * q_tiles;
   if (total == 0) return hipSuccess;
-  const int64_t per_xcd = (total + 7) / 8;
-  const dim3 grid(static_cast<uint32_t>(per_xcd * 8));
+  const dim3 grid(static_cast<uint32_t>(total));
   if (a.head_dim == 128) {
     hipLaunchKernelGGL(varlen_prefill_kernel<128>, grid, dim3(kPfThreads), 0, stream, a,
-                       heads_per_wg, head_groups, rows_per_wg, q_tiles, total, per_xcd);
+                       heads_per_wg, head_groups, rows_per_wg, q_tiles);
   } else {
     hipLaunchKernelGGL(varlen_prefill_kernel<64>, grid, dim3(kPfThreads), 0, stream, a,
-                       heads_per_wg, head_groups, rows_per_wg, q_tiles, total, per_xcd);
+                       heads_per_wg, head_groups, rows_per_wg, q_tiles);
   }
   return hipGetLastError();
 }
