@@ -74,15 +74,94 @@ def kernel_sources_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+# Kernels that make up one call of each boundary entry point (rocprofv3 names).
+CALL_KERNELS = {
+    "paged_decode_attention": ("paged_decode_kernel", "paged_decode_combine_kernel"),
+    "varlen_prefill_attention": ("varlen_prefill_kernel",),
+    "store_kvcache": ("store_kvcache_kernel",),
+}
+COPY_PROBE_BYTES = 1 << 30  # plain device-to-device copy that calibrates the counters
+COPY_KERNEL = "copyBuffer"
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def measured_traffic(workload: str, call: str):
+    """HBM bytes per call from committed rocprofv3 counter runs, if still current."""
+    p = traffic_path(workload)
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
     if rec.get("kernel_sources_sha") != kernel_sources_sha():
         return None
-    return rec.get("kernels", {}).get(kernel, {}).get("hbm_bytes_per_launch")
+    return rec.get("calls", {}).get(call, {}).get("hbm_bytes_per_call")
+
+
+def _counter_values(run_dir: str, counter: str):
+    """{kernel name: [(dispatch id, value), ...]} for `counter` in a rocprofv3 csv run."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    by_kernel = {}
+    for (name, did), v in per.items():
+        by_kernel.setdefault(name, []).append((did, v))
+    return by_kernel
+
+
+def _copy_probe_kib(table) -> float:
+    """Counter value of the calibration copy: the last three copy dispatches."""
+    copies = sorted((did, v) for n, dv in table.items() if COPY_KERNEL in n for did, v in dv)
+    if len(copies) < 3:
+        raise SystemExit("no copy probe in the counter run (run bench.py with --copy-probe)")
+    last = [v for _, v in copies[-3:]]
+    if max(last) > 1.05 * min(last):
+        raise SystemExit(f"inconsistent copy probe readings {last}")
+    return sum(last) / 3.0
+
+
+def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
+    """Per-call HBM traffic from a FETCH_SIZE run and a WRITE_SIZE run.
+
+    Both counters read in KiB per dispatch; each is scaled by what it reads for
+    the 1 GiB device copy that the profiled run ends with (the largest copy
+    dispatch), so the result is in true bytes.  Writes profiles/traffic_<w>.json.
+    """
+    fetch = _counter_values(fetch_dir, "FETCH_SIZE")
+    write = _counter_values(write_dir, "WRITE_SIZE")
+    fetch_scale = COPY_PROBE_BYTES / (_copy_probe_kib(fetch) * 1024.0)
+    write_scale = COPY_PROBE_BYTES / (_copy_probe_kib(write) * 1024.0)
+
+    def mean(dv):
+        return sum(v for _, v in dv) / len(dv)
+
+    calls = {}
+    for call, kernels in CALL_KERNELS.items():
+        f = [(n, mean(dv)) for n, dv in fetch.items() if any(k in n for k in kernels)]
+        w = [(n, mean(dv)) for n, dv in write.items() if any(k in n for k in kernels)]
+        if not f:
+            continue
+        rb = sum(v for _, v in f) * 1024.0 * fetch_scale
+        wb = sum(v for _, v in w) * 1024.0 * write_scale
+        calls[call] = {"fetch_kib_per_call": sum(v for _, v in f),
+                       "write_kib_per_call": sum(v for _, v in w),
+                       "read_bytes_per_call": rb, "write_bytes_per_call": wb,
+                       "hbm_bytes_per_call": rb + wb,
+                       "kernels": sorted({k for n, _ in f for k in kernels if k in n})}
+    rec = {"workload": workload, "kernel_sources_sha": kernel_sources_sha(),
+           "copy_probe_bytes": COPY_PROBE_BYTES,
+           "fetch_scale": fetch_scale, "write_scale": write_scale, "calls": calls}
+    with open(traffic_path(workload), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return rec
 
 
 # ---- CPU baseline: the fp64 oracle on a bounded sample ----------------------------------
@@ -136,7 +215,15 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0, help="decode split (0 = library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="end with a 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/traffic_<workload>.json")
     args = ap.parse_args()
+
+    if args.counters:
+        print(json.dumps(summarize_counters(args.workload, *args.counters)), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -247,6 +334,13 @@ def main():
         rec["store_gbs"] = store_bytes(w) / (store_ms * 1e-3) / 1e9
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(rec), flush=True)
 
 
