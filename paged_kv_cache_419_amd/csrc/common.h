@@ -69,13 +69,13 @@ __device__ __forceinline__ void lds_dma16(const void* src, lds_bytes dst) {
 }
 
 // Workgroup barrier once at most N vector-memory loads of this wave are still
-// outstanding (direct-to-LDS loads included): this wave's older loads have
-// landed, younger ones stay in flight.  One asm statement with a memory
+// outstanding (direct-to-LDS loads included) and its LDS accesses are done:
+// this wave's older loads have landed, younger ones stay in flight.  One asm statement with a memory
 // clobber, so the compiler moves no memory access across it.
 template <int N>
 __device__ __forceinline__ void barrier_after_loads() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier once this wave's LDS accesses have completed.

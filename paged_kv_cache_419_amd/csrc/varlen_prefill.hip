@@ -12,10 +12,11 @@
 // waves cover up to four query heads of that kv head and 32 query rows each
 // (4 heads x 32 rows at GQA ratio 4, 2 x 64 at ratio 2, 1 x 128 without GQA),
 // so one K/V tile in LDS serves 128 (row, head) pairs.  Work items are ordered
-// q tile (latest first: those rows see the most keys), then sequence, then kv
+// sequence, then q tile (latest first: those rows see the most keys), then kv
 // head; workgroups go round-robin to the 8 XCDs, so with 8 | Hkv every XCD
-// serves one kv head and keeps that head's K/V (a shared prefix especially)
-// in its own L2.
+// serves one kv head, and the q tiles of a sequence run close together in
+// time on that XCD: the sequence's K/V for that head (and a shared prefix)
+// stay in the XCD's L2 instead of being read from HBM once per q tile.
 //
 // Pipeline.  K and V tiles of 64 keys go straight from HBM into LDS with the
 // gfx950 direct-to-LDS loads (global_load_lds_dwordx4), double-buffered: the
@@ -40,8 +41,11 @@ namespace {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfStages = 2;  // K/V tiles resident in LDS: the current one + 1 in flight
 constexpr int kPfKeys = 64;  // keys per tile
 constexpr int kPfRows = 32;  // query rows per wave (the N side of a 32x32 MFMA)
+constexpr float kRescaleSlack = 8.f;  // log2 headroom of the lazy softmax rescale
+constexpr unsigned short kSlackBf16Bits = 0x4380;  // bf16 bit pattern of 2^kRescaleSlack
 
 template <int D>
 struct PrefillShape {
@@ -102,9 +106,46 @@ template <int D>
 struct WaveState {
   u32x4 qb[PrefillShape<D>::KS];      // B operand Q^T per k-step
   f32x16 o[PrefillShape<D>::DC];      // O^T accumulators
-  float m;                            // running max (log2 domain) of this lane's row
-  float l;                            // running sum over this lane's half of the keys
+  f32x16 lsum;                        // row sums of the bf16 weights (every element of a lane's column alike)
+  float m;                            // running reference max (log2 domain) of this lane's row
 };
+
+// Weights exp2(s c - m) of one 64-key tile, rounded to bf16 and packed in
+// the B-operand order of the PV product: 16-key block u = 2 kb + hb, k-slots
+// 0..3 are keys 16u + 4h + i, k-slots 4..7 are keys 16u + 8 + 4h + i.
+__device__ __forceinline__ void tile_weights(const f32x16 (&s)[2], u32x4 (&pb)[4], float m, float c) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = fast_exp2(__builtin_fmaf(s[kb][v], c, -m));
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int j = 2 * hb;
+      pb[2 * kb + hb] = u32x4{pack_bf16x2(p[4 * j], p[4 * j + 1]), pack_bf16x2(p[4 * j + 2], p[4 * j + 3]),
+                              pack_bf16x2(p[4 * j + 4], p[4 * j + 5]),
+                              pack_bf16x2(p[4 * j + 6], p[4 * j + 7])};
+    }
+  }
+}
+
+// True when some packed bf16 weight is >= 2^kRescaleSlack (or inf / NaN):
+// weights are non-negative, so their bit patterns order like their values;
+// a packed 16-bit max folds two weights per instruction.
+__device__ __forceinline__ bool weights_overflow(const u32x4 (&pb)[4]) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mx = __builtin_bit_cast(u16x2, pb[0][0]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (u != 0 || e != 0) {
+        const u16x2 v = __builtin_bit_cast(u16x2, pb[u][e]);
+        mx = __builtin_elementwise_max(mx, v);
+      }
+  const unsigned short lim = kSlackBf16Bits;
+  return (mx[0] >= lim) || (mx[1] >= lim);
+}
 
 // One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 template <int D>
@@ -132,39 +173,42 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
       for (int v = 0; v < 16; ++v)
         if (k0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3) > lim) s[kb][v] = -INFINITY;
   }
-  float mx = s[0][0];
+  // Weights p = exp2(s c - m) against the running reference m.  m only has
+  // to bound the scores loosely: the weights are consistent with the sums and
+  // O whatever m is.  It is first set from the first tile's max; afterwards
+  // the max is not computed at all: the tile's weights are checked instead,
+  // and only when some weight reaches 2^kRescaleSlack (its row's max rose by
+  // that much, rare after the first tiles) is m raised and O rescaled.
+  if (__ballot(w.m == -INFINITY) != 0) {  // first tile of this wave
+    float mx = s[0][0];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(w.m, mx * c);
-  if (__ballot(m_new > w.m) != 0) {  // rescale only when some running max grew
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    w.m = mx * c;
+  }
+  u32x4 pb[4];
+  tile_weights(s, pb, w.m, c);
+  if (__ballot(weights_overflow(pb)) != 0) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(w.m, mx * c);
     const float alpha = fast_exp2(w.m - m_new);
-    w.l *= alpha;
+    w.lsum *= alpha;
 #pragma unroll
     for (int cb = 0; cb < S::DC; ++cb) w.o[cb] *= alpha;
     w.m = m_new;
+    tile_weights(s, pb, w.m, c);
   }
-  u32x4 pb[4];
+  // row sums on the matrix cores: (all-ones)^T P^T
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    float p[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      p[v] = fast_exp2(__builtin_fmaf(s[kb][v], c, -w.m));
-      w.l += p[v];
-    }
-    // 16-key block u = 2 kb + hb: k-slots 0..3 are keys 16u + 4h + i,
-    // k-slots 4..7 are keys 16u + 8 + 4h + i
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int j = 2 * hb;
-      pb[2 * kb + hb] = u32x4{pack_bf16x2(p[4 * j], p[4 * j + 1]), pack_bf16x2(p[4 * j + 2], p[4 * j + 3]),
-                              pack_bf16x2(p[4 * j + 4], p[4 * j + 5]),
-                              pack_bf16x2(p[4 * j + 6], p[4 * j + 7])};
-    }
-  }
+  for (int u = 0; u < 4; ++u) w.lsum = mfma32x32x16(ones, pb[u], w.lsum);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -181,17 +225,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
     PrefillArgs a, int32_t heads_per_wg, int32_t head_groups, int32_t rows_per_wg,
     int32_t q_tiles) {
   using S = PrefillShape<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char buf_a[2 * S::TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char buf_b[2 * S::TILE];
+  // kPfStages slots, each a K tile followed by a V tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kPfStages * 2 * S::TILE];
 
-  // item = ((q tile rank * num_seqs + seq) * Hkv + g) * head_groups + hg
+  // item = ((seq * q_tiles + q tile rank) * Hkv + g) * head_groups + hg
   int64_t rest = blockIdx.x;
   const int hg = static_cast<int>(rest % head_groups);
   rest /= head_groups;
   const int g = static_cast<int>(rest % a.num_kv_heads);
   rest /= a.num_kv_heads;
-  const int seq = static_cast<int>(rest % a.num_seqs);
-  const int qtile = q_tiles - 1 - static_cast<int>(rest / a.num_seqs);
+  const int qtile = q_tiles - 1 - static_cast<int>(rest % q_tiles);
+  const int seq = static_cast<int>(rest / q_tiles);
 
   const int q_start = a.cu_q[seq];
   const int lq = a.cu_q[seq + 1] - q_start;
@@ -218,15 +262,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
           static_cast<int64_t>(seq) * a.max_blocks_per_seq;
   sv.lk = lk;
   sv.shift = a.block_shift;
-  lds_bytes ka = (lds_bytes)buf_a;
-  lds_bytes va = (lds_bytes)buf_a + S::TILE;
-  lds_bytes kb_ = (lds_bytes)buf_b;
-  lds_bytes vb = (lds_bytes)buf_b + S::TILE;
+  const lds_bytes lbase = (lds_bytes)smem;
+  auto kslot = [&](int t) { return lbase + (t % kPfStages) * (2 * S::TILE); };
+  auto vslot = [&](int t) { return lbase + (t % kPfStages) * (2 * S::TILE) + S::TILE; };
 
   const int last_row = min(r0 + rows_per_wg, lq) - 1;
   const int kend = a.causal ? min(lk, off + last_row + 1) : lk;
   const int n_tiles = (kend + kPfKeys - 1) / kPfKeys;
-  if (n_tiles > 0) issue_tile<D>(sv, 0, wave, lane, ka, va);
+  for (int t = 0; t < min(n_tiles, kPfStages - 1); ++t)
+    issue_tile<D>(sv, t * kPfKeys, wave, lane, kslot(t), vslot(t));
 
   WaveState<D> w;
   // With a negative scale, negate Q (exact in bf16) and use |scale|, so the
@@ -251,7 +295,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
 #pragma unroll
   for (int cb = 0; cb < S::DC; ++cb) w.o[cb] = f32x16{};
   w.m = -INFINITY;
-  w.l = 0.f;
+  w.lsum = f32x16{};
 
   // last visible key of this lane's row (padding rows borrow the last row's)
   const int lim = a.causal ? min(off + min(row, lq - 1), lk - 1) : lk - 1;
@@ -276,42 +320,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
     }
   }
 
-  // Double-buffered tile loop (unrolled by two so each LDS buffer is a
-  // distinct array and the compiler never waits on the other buffer's loads).
-  // Before the first barrier of a tile each wave waits for its own loads of
-  // that tile (the next tile's stay in flight); the second barrier keeps the
-  // buffer from being refilled while another wave still reads it.
-  constexpr int kInFlight = 2 * S::LOADS;
-  for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) {
-      issue_tile<D>(sv, (t + 1) * kPfKeys, wave, lane, kb_, vb);
-      barrier_after_loads<kInFlight>();
-    } else {
-      barrier_after_loads<0>();
+  // Tile loop over a ring of kPfStages LDS slots, one barrier per tile: each
+  // wave waits for its own loads of tile t (younger tiles stay in flight) and
+  // for its LDS reads of tile t - 1, the workgroup syncs, and only then is
+  // tile t + kPfStages - 1 issued into the slot tile t - 1 has just freed.
+  for (int t = 0; t < n_tiles; ++t) {
+    switch (min(n_tiles - 1 - t, kPfStages - 2)) {  // tiles younger than t in flight
+      case 2: barrier_after_loads<2 * 2 * S::LOADS>(); break;
+      case 1: barrier_after_loads<1 * 2 * S::LOADS>(); break;
+      default: barrier_after_loads<0>(); break;
     }
-    {
-      const int k0 = t * kPfKeys;
-      if (hvalid && k0 <= lim_hi)
-        compute_tile<D>(w, ka, va, kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
-    }
-    barrier_after_lds();
-    if (t + 1 >= n_tiles) break;
-    if (t + 2 < n_tiles) {
-      issue_tile<D>(sv, (t + 2) * kPfKeys, wave, lane, ka, va);
-      barrier_after_loads<kInFlight>();
-    } else {
-      barrier_after_loads<0>();
-    }
-    {
-      const int k0 = (t + 1) * kPfKeys;
-      if (hvalid && k0 <= lim_hi)
-        compute_tile<D>(w, kb_, vb, kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
-    }
-    barrier_after_lds();
+    const int tn = t + kPfStages - 1;
+    if (tn < n_tiles) issue_tile<D>(sv, tn * kPfKeys, wave, lane, kslot(tn), vslot(tn));
+    const int k0 = t * kPfKeys;
+    if (hvalid && k0 <= lim_hi)
+      compute_tile<D>(w, kslot(t), vslot(t), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
   }
 
   if (!hvalid || row >= lq) return;
-  const float lt = w.l + __shfl_xor(w.l, 32);
+  const float lt = w.lsum[0];  // the sum over all keys of this lane's row
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   uint16_t* op = static_cast<uint16_t*>(a.out) +
                  (static_cast<int64_t>(q_start + row) * a.num_q_heads + head) * D + 4 * h;
