@@ -75,30 +75,77 @@ struct SeqView {
   uint32_t row_bytes;
 };
 
-// Issue this wave's share of the K and V tile starting at key k0 into LDS
-// (rows 16 * wave .. 16 * wave + 15 of each tile).
+// Each wave loads rows 16 * wave .. 16 * wave + 15 of every K and V tile.
+// Those 16 rows lie in one cache block (blocks hold >= 16 tokens and the rows
+// start at a multiple of 16), so one block-table entry addresses them; rows
+// past Lk are redirected to key Lk - 1, which then lies in that same block or
+// is the only key loaded.
+constexpr int kPfWaveRows = kPfKeys / kPfWaves;
+
+// Block-table entry of this wave's rows of the tile starting at key k0 (a
+// scalar load; issued one tile ahead of its use).
+__device__ __forceinline__ int64_t tile_block(const SeqView& sv, int k0, int wave) {
+  return sv.bt[min(k0 + wave * kPfWaveRows, sv.lk - 1) >> sv.shift];
+}
+
+// Per-lane byte offsets, inside a block, of this wave's direct-to-LDS loads of
+// one tile, relative to the wave's first row: lane (row rr = lane / CH of
+// load e, LDS position p = lane % CH) reads the chunk stored at p.
 template <int D>
-__device__ __forceinline__ void issue_tile(const SeqView& sv, int k0, int wave, int lane,
-                                           lds_bytes kdst, lds_bytes vdst) {
+struct TileLoadOffsets {
+  uint32_t k[PrefillShape<D>::LOADS];
+  uint32_t v[PrefillShape<D>::LOADS];
+};
+
+template <int D>
+__device__ __forceinline__ TileLoadOffsets<D> tile_load_offsets(int lane, int wave, uint32_t row_bytes) {
   using S = PrefillShape<D>;
-  const int bmask = (1 << sv.shift) - 1;
-  // The wave's 16 rows lie in one cache block (blocks hold >= 16 tokens and
-  // the rows start at a multiple of 16); rows past Lk are redirected to key
-  // Lk - 1, which then lies in that same block or is the only key loaded.
-  const int kfirst = min(k0 + wave * (kPfKeys / kPfWaves), sv.lk - 1);
-  const int64_t blk = sv.bt[kfirst >> sv.shift];
-  const int64_t base = (blk << sv.shift) * static_cast<int64_t>(sv.row_bytes);
+  TileLoadOffsets<D> t;
 #pragma unroll
   for (int e = 0; e < S::LOADS; ++e) {
-    const int rr0 = wave * (kPfKeys / kPfWaves) + e * S::RPL;  // first row of this load
-    const int rr = rr0 + lane / S::CH;
+    const int rel = e * S::RPL + lane / S::CH;  // row inside the wave's 16
+    const int rr = wave * kPfWaveRows + rel;     // row inside the tile
     const int p = lane % S::CH;
-    const int kcl = min(k0 + rr, sv.lk - 1);
-    const uint32_t roff = static_cast<uint32_t>(kcl & bmask) * sv.row_bytes;
-    const char* ksrc = reinterpret_cast<const char*>(sv.kc) + base + roff + 16 * (p ^ kswz<D>(rr));
-    const char* vsrc = reinterpret_cast<const char*>(sv.vc) + base + roff + 16 * (p ^ vswz<D>(rr));
-    lds_dma16(ksrc, kdst + rr0 * S::ROWB);
-    lds_dma16(vsrc, vdst + rr0 * S::ROWB);
+    t.k[e] = rel * row_bytes + 16 * (p ^ kswz<D>(rr));
+    t.v[e] = rel * row_bytes + 16 * (p ^ vswz<D>(rr));
+  }
+  return t;
+}
+
+// Issue this wave's share of the K and V tile starting at key k0 into LDS;
+// blk is tile_block(sv, k0, wave).
+template <int D>
+__device__ __forceinline__ void issue_tile(const SeqView& sv, int64_t blk, int k0, int wave, int lane,
+                                           const TileLoadOffsets<D>& lo, lds_bytes kdst,
+                                           lds_bytes vdst) {
+  using S = PrefillShape<D>;
+  const int bmask = (1 << sv.shift) - 1;
+  const int r0 = k0 + wave * kPfWaveRows;  // first key of this wave's rows
+  if (r0 + kPfWaveRows <= sv.lk) {
+    // all 16 rows live: scalar base plus the constant per-lane offsets
+    const int64_t base = ((blk << sv.shift) + (r0 & bmask)) * static_cast<int64_t>(sv.row_bytes);
+    const char* kb = reinterpret_cast<const char*>(sv.kc) + base;
+    const char* vb = reinterpret_cast<const char*>(sv.vc) + base;
+#pragma unroll
+    for (int e = 0; e < S::LOADS; ++e) {
+      const int rr0 = wave * kPfWaveRows + e * S::RPL;
+      lds_dma16(kb + lo.k[e], kdst + rr0 * S::ROWB);
+      lds_dma16(vb + lo.v[e], vdst + rr0 * S::ROWB);
+    }
+  } else {
+    const int64_t base = (blk << sv.shift) * static_cast<int64_t>(sv.row_bytes);
+#pragma unroll
+    for (int e = 0; e < S::LOADS; ++e) {
+      const int rr0 = wave * kPfWaveRows + e * S::RPL;  // first row of this load
+      const int rr = rr0 + lane / S::CH;
+      const int p = lane % S::CH;
+      const int kcl = min(k0 + rr, sv.lk - 1);
+      const uint32_t roff = static_cast<uint32_t>(kcl & bmask) * sv.row_bytes;
+      const char* ksrc = reinterpret_cast<const char*>(sv.kc) + base + roff + 16 * (p ^ kswz<D>(rr));
+      const char* vsrc = reinterpret_cast<const char*>(sv.vc) + base + roff + 16 * (p ^ vswz<D>(rr));
+      lds_dma16(ksrc, kdst + rr0 * S::ROWB);
+      lds_dma16(vsrc, vdst + rr0 * S::ROWB);
+    }
   }
 }
 
@@ -109,6 +156,21 @@ struct WaveState {
   f32x16 lsum;                        // row sums of the bf16 weights (every element of a lane's column alike)
   float m;                            // running reference max (log2 domain) of this lane's row
 };
+
+// Scheduling shape for a block of N MFMAs fed by LDS reads (R reads per
+// MFMA, the first AHEAD reads issued before any MFMA): keeps AHEAD reads in
+// flight so the matrix core does not wait on LDS latency.  MFMAs that take no
+// LDS operand (the row-sum products) just fill slots.
+template <int N, int AHEAD, int R>
+__device__ __forceinline__ void sched_reads_ahead() {
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+}
 
 // Weights exp2(s c - m) of one 64-key tile, rounded to bf16 and packed in
 // the B-operand order of the PV product: 16-key block u = 2 kb + hb, k-slots
@@ -165,6 +227,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
       s[kb] = mfma32x32x16(a, w.qb[ks], s[kb]);
     }
   }
+  // Keep several K operand reads in flight ahead of the MFMAs (LDS latency is
+  // a few MFMA issue slots).
+  sched_reads_ahead<2 * S::KS, 4, 1>();
   // element 4j + i of s[kb] is key k0 + 32 kb + 8 j + 4 h + i of this lane's row
   if (need_mask) {
 #pragma unroll
@@ -218,6 +283,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
       w.o[cb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[u], w.o[cb]);
     }
   }
+  sched_reads_ahead<4 * S::DC + 4, 8, 2>();
 }
 
 template <int D>
@@ -269,8 +335,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
   const int last_row = min(r0 + rows_per_wg, lq) - 1;
   const int kend = a.causal ? min(lk, off + last_row + 1) : lk;
   const int n_tiles = (kend + kPfKeys - 1) / kPfKeys;
+  const TileLoadOffsets<D> lo = tile_load_offsets<D>(lane, wave, sv.row_bytes);
   for (int t = 0; t < min(n_tiles, kPfStages - 1); ++t)
-    issue_tile<D>(sv, t * kPfKeys, wave, lane, kslot(t), vslot(t));
+    issue_tile<D>(sv, tile_block(sv, t * kPfKeys, wave), t * kPfKeys, wave, lane, lo, kslot(t), vslot(t));
+  // block of the next tile to issue, looked up one tile ahead
+  int64_t blk_next = n_tiles >= kPfStages ? tile_block(sv, (kPfStages - 1) * kPfKeys, wave) : 0;
 
   WaveState<D> w;
   // With a negative scale, negate Q (exact in bf16) and use |scale|, so the
@@ -331,7 +400,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
       default: barrier_after_loads<0>(); break;
     }
     const int tn = t + kPfStages - 1;
-    if (tn < n_tiles) issue_tile<D>(sv, tn * kPfKeys, wave, lane, kslot(tn), vslot(tn));
+    if (tn < n_tiles) {
+      issue_tile<D>(sv, blk_next, tn * kPfKeys, wave, lane, lo, kslot(tn), vslot(tn));
+      if (tn + 1 < n_tiles) blk_next = tile_block(sv, (tn + 1) * kPfKeys, wave);
+    }
     const int k0 = t * kPfKeys;
     if (hvalid && k0 <= lim_hi)
       compute_tile<D>(w, kslot(t), vslot(t), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
