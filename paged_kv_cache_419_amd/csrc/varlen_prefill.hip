@@ -43,6 +43,8 @@ constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfStages = 2;  // K/V tiles resident in LDS: the current one + 1 in flight
 constexpr int kPfKeys = 64;  // keys per tile
+constexpr int kPfKB = kPfKeys / 32;  // 32-key MFMA blocks per tile
+constexpr int kPfU = kPfKeys / 16;   // 16-key k-blocks of the PV product per tile
 constexpr int kPfRows = 32;  // query rows per wave (the N side of a 32x32 MFMA)
 constexpr float kRescaleSlack = 8.f;  // log2 headroom of the lazy softmax rescale
 constexpr unsigned short kSlackBf16Bits = 0x4380;  // bf16 bit pattern of 2^kRescaleSlack
@@ -157,27 +159,36 @@ struct WaveState {
   float m;                            // running reference max (log2 domain) of this lane's row
 };
 
-// Scheduling shape for a block of N MFMAs fed by LDS reads (R reads per
-// MFMA, the first AHEAD reads issued before any MFMA): keeps AHEAD reads in
-// flight so the matrix core does not wait on LDS latency.  MFMAs that take no
-// LDS operand (the row-sum products) just fill slots.
-template <int N, int AHEAD, int R>
+// Scheduling shape for a block of M MFMAs fed by NR LDS reads: the first
+// AHEAD reads go out before any MFMA, then each MFMA is followed by the next
+// reads (evenly spread), so AHEAD reads stay in flight and the matrix core
+// does not wait on LDS latency.
+template <int M, int NR, int AHEAD>
 __device__ __forceinline__ void sched_reads_ahead() {
+  static_assert(AHEAD <= NR, "more reads ahead than reads");
+  constexpr int kRest = NR - AHEAD;
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  constexpr int kPer = (kRest + M - 1) / M > 0 ? (kRest + M - 1) / M : 1;
+  constexpr int kFull = kRest / kPer;  // MFMAs followed by kPer reads
+  constexpr int kRem = kRest % kPer;   // reads after MFMA number kFull
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
+  for (int i = 0; i < M; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    if (i < kFull) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);
+    } else if (i == kFull && kRem > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kRem, 0);
+    }
   }
 }
 
 // Weights exp2(s c - m) of one 64-key tile, rounded to bf16 and packed in
 // the B-operand order of the PV product: 16-key block u = 2 kb + hb, k-slots
 // 0..3 are keys 16u + 4h + i, k-slots 4..7 are keys 16u + 8 + 4h + i.
-__device__ __forceinline__ void tile_weights(const f32x16 (&s)[2], u32x4 (&pb)[4], float m, float c) {
+__device__ __forceinline__ void tile_weights(const f32x16 (&s)[kPfKB], u32x4 (&pb)[kPfU], float m, float c) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < kPfKB; ++kb) {
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = fast_exp2(__builtin_fmaf(s[kb][v], c, -m));
@@ -194,11 +205,11 @@ __device__ __forceinline__ void tile_weights(const f32x16 (&s)[2], u32x4 (&pb)[4
 // True when some packed bf16 weight is >= 2^kRescaleSlack (or inf / NaN):
 // weights are non-negative, so their bit patterns order like their values;
 // a packed 16-bit max folds two weights per instruction.
-__device__ __forceinline__ bool weights_overflow(const u32x4 (&pb)[4]) {
+__device__ __forceinline__ bool weights_overflow(const u32x4 (&pb)[kPfU]) {
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   u16x2 mx = __builtin_bit_cast(u16x2, pb[0][0]);
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < kPfU; ++u)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (u != 0 || e != 0) {
@@ -217,9 +228,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
                                              int k0, int lim, bool need_mask, int h,
                                              float c) {
   using S = PrefillShape<D>;
-  f32x16 s[2];
+  f32x16 s[kPfKB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < kPfKB; ++kb) {
     s[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) {
@@ -229,11 +240,11 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
   }
   // Keep several K operand reads in flight ahead of the MFMAs (LDS latency is
   // a few MFMA issue slots).
-  sched_reads_ahead<2 * S::KS, 4, 1>();
+  sched_reads_ahead<kPfKB * S::KS, kPfKB * S::KS, 4>();
   // element 4j + i of s[kb] is key k0 + 32 kb + 8 j + 4 h + i of this lane's row
   if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kPfKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         if (k0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3) > lim) s[kb][v] = -INFINITY;
@@ -247,18 +258,18 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
   if (__ballot(w.m == -INFINITY) != 0) {  // first tile of this wave
     float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kPfKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     w.m = mx * c;
   }
-  u32x4 pb[4];
+  u32x4 pb[kPfU];
   tile_weights(s, pb, w.m, c);
   if (__ballot(weights_overflow(pb)) != 0) {
     float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kPfKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -273,9 +284,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
   // row sums on the matrix cores: (all-ones)^T P^T
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
-  for (int u = 0; u < 4; ++u) w.lsum = mfma32x32x16(ones, pb[u], w.lsum);
+  for (int u = 0; u < kPfU; ++u) w.lsum = mfma32x32x16(ones, pb[u], w.lsum);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kPfU; ++u) {
 #pragma unroll
     for (int cb = 0; cb < S::DC; ++cb) {
       const uint2 lo = lds_read_tr16(vt + vaddr[cb] + 16 * u * S::ROWB);
@@ -283,7 +294,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
       w.o[cb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[u], w.o[cb]);
     }
   }
-  sched_reads_ahead<4 * S::DC + 4, 8, 2>();
+  sched_reads_ahead<kPfU * S::DC + kPfU, 2 * kPfU * S::DC, 8>();
 }
 
 template <int D>
@@ -393,6 +404,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
   // wave waits for its own loads of tile t (younger tiles stay in flight) and
   // for its LDS reads of tile t - 1, the workgroup syncs, and only then is
   // tile t + kPfStages - 1 issued into the slot tile t - 1 has just freed.
+#pragma unroll 1
   for (int t = 0; t < n_tiles; ++t) {
     switch (min(n_tiles - 1 - t, kPfStages - 2)) {  // tiles younger than t in flight
       case 2: barrier_after_loads<2 * 2 * S::LOADS>(); break;
