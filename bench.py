@@ -65,10 +65,20 @@ def prefill_bytes(w) -> int:
     return qo + kv
 
 
-def kernel_sources_sha() -> str:
+# Source files whose change invalidates the counters of each call's kernels.
+CALL_SOURCES = {
+    "paged_decode_attention": ("paged_decode.hip",),
+    "varlen_prefill_attention": ("varlen_prefill.hip",),
+    "store_kvcache": ("store_kvcache.hip",),
+}
+SHARED_SOURCES = ("common.h", "kernels.h")
+
+
+def kernel_sources_sha(call: str) -> str:
+    """Hash of the sources that define one call's kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_419_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(CALL_SOURCES[call] + SHARED_SOURCES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -93,10 +103,10 @@ def measured_traffic(workload: str, call: str):
     p = traffic_path(workload)
     if not os.path.exists(p):
         return None
-    rec = json.load(open(p))
-    if rec.get("kernel_sources_sha") != kernel_sources_sha():
+    rec = json.load(open(p)).get("calls", {}).get(call, {})
+    if rec.get("kernel_sources_sha") != kernel_sources_sha(call):
         return None
-    return rec.get("calls", {}).get(call, {}).get("hbm_bytes_per_call")
+    return rec.get("hbm_bytes_per_call")
 
 
 def _counter_values(run_dir: str, counter: str):
@@ -154,9 +164,9 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
                        "write_kib_per_call": sum(v for _, v in w),
                        "read_bytes_per_call": rb, "write_bytes_per_call": wb,
                        "hbm_bytes_per_call": rb + wb,
-                       "kernels": sorted({k for n, _ in f for k in kernels if k in n})}
-    rec = {"workload": workload, "kernel_sources_sha": kernel_sources_sha(),
-           "copy_probe_bytes": COPY_PROBE_BYTES,
+                       "kernels": sorted({k for n, _ in f for k in kernels if k in n}),
+                       "kernel_sources_sha": kernel_sources_sha(call)}
+    rec = {"workload": workload, "copy_probe_bytes": COPY_PROBE_BYTES,
            "fetch_scale": fetch_scale, "write_scale": write_scale, "calls": calls}
     with open(traffic_path(workload), "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -215,6 +225,8 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0, help="decode split (0 = library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: also time the step replayed from a captured HIP graph")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with a 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -328,6 +340,27 @@ def main():
     }
     if decode:
         rec["decode_tok_per_s"] = w.num_seqs / (ms_step * 1e-3)
+        if args.graph:
+            # the same step (store + decode) captured once per input copy and replayed
+            graphs = []
+            for i, c in enumerate(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    store(c)
+                    attend(c, outs[i])
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % reps].replay()
+            torch.cuda.synchronize()
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
+            for i in range(args.steps):
+                graphs[i % reps].replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            rec["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
+            rec["graph_decode_tok_per_s"] = w.num_seqs / (rec["graph_ms_per_step"] * 1e-3)
         rec["hbm_frac"] = value / HBM_PEAK_GBS
     else:
         rec["mfma_frac"] = value / MFMA_BF16_PEAK_TFLOPS

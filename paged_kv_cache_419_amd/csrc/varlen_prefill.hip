@@ -297,6 +297,37 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
   sched_reads_ahead<kPfU * S::DC + kPfU, 2 * kPfU * S::DC, 8>();
 }
 
+// Start of tile step t: wait for this wave's loads of tile t (younger tiles
+// stay in flight) and for its LDS reads of tile t - 1, sync the workgroup,
+// then issue tile t + kPfStages - 1 into the slot tile t - 1 has just freed.
+// blk_next carries the block-table entry of that tile, looked up a step ahead.
+template <int D>
+__device__ __forceinline__ lds_bytes kslot_of(lds_bytes lbase, int t) {
+  return lbase + (t % kPfStages) * (2 * PrefillShape<D>::TILE);
+}
+template <int D>
+__device__ __forceinline__ lds_bytes vslot_of(lds_bytes lbase, int t) {
+  return kslot_of<D>(lbase, t) + PrefillShape<D>::TILE;
+}
+
+template <int D>
+__device__ __forceinline__ void tile_sync_and_issue(const SeqView& sv, int t, int n_tiles, int wave,
+                                                    int lane, const TileLoadOffsets<D>& lo,
+                                                    int64_t& blk_next, lds_bytes lbase) {
+  using S = PrefillShape<D>;
+  switch (min(n_tiles - 1 - t, kPfStages - 2)) {  // tiles younger than t in flight
+    case 2: barrier_after_loads<2 * 2 * S::LOADS>(); break;
+    case 1: barrier_after_loads<1 * 2 * S::LOADS>(); break;
+    default: barrier_after_loads<0>(); break;
+  }
+  const int tn = t + kPfStages - 1;
+  if (tn < n_tiles) {
+    issue_tile<D>(sv, blk_next, tn * kPfKeys, wave, lane, lo, kslot_of<D>(lbase, tn),
+                  vslot_of<D>(lbase, tn));
+    if (tn + 1 < n_tiles) blk_next = tile_block(sv, (tn + 1) * kPfKeys, wave);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
     PrefillArgs a, int32_t heads_per_wg, int32_t head_groups, int32_t rows_per_wg,
@@ -340,8 +371,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
   sv.lk = lk;
   sv.shift = a.block_shift;
   const lds_bytes lbase = (lds_bytes)smem;
-  auto kslot = [&](int t) { return lbase + (t % kPfStages) * (2 * S::TILE); };
-  auto vslot = [&](int t) { return lbase + (t % kPfStages) * (2 * S::TILE) + S::TILE; };
+  auto kslot = [&](int t) { return kslot_of<D>(lbase, t); };
+  auto vslot = [&](int t) { return vslot_of<D>(lbase, t); };
 
   const int last_row = min(r0 + rows_per_wg, lq) - 1;
   const int kend = a.causal ? min(lk, off + last_row + 1) : lk;
@@ -404,22 +435,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
   // wave waits for its own loads of tile t (younger tiles stay in flight) and
   // for its LDS reads of tile t - 1, the workgroup syncs, and only then is
   // tile t + kPfStages - 1 issued into the slot tile t - 1 has just freed.
+  // Tiles past lim_hi hold no key any row of this wave sees (they exist for
+  // other row blocks of the workgroup); padding heads compute nothing.  The
+  // computing tiles come first, in a loop of their own, so the accumulators
+  // are updated unconditionally inside it.
+  const int n_compute = hvalid ? min(n_tiles, lim_hi / kPfKeys + 1) : 0;
+  int t = 0;
 #pragma unroll 1
-  for (int t = 0; t < n_tiles; ++t) {
-    switch (min(n_tiles - 1 - t, kPfStages - 2)) {  // tiles younger than t in flight
-      case 2: barrier_after_loads<2 * 2 * S::LOADS>(); break;
-      case 1: barrier_after_loads<1 * 2 * S::LOADS>(); break;
-      default: barrier_after_loads<0>(); break;
-    }
-    const int tn = t + kPfStages - 1;
-    if (tn < n_tiles) {
-      issue_tile<D>(sv, blk_next, tn * kPfKeys, wave, lane, lo, kslot(tn), vslot(tn));
-      if (tn + 1 < n_tiles) blk_next = tile_block(sv, (tn + 1) * kPfKeys, wave);
-    }
+  for (; t < n_compute; ++t) {
+    tile_sync_and_issue<D>(sv, t, n_tiles, wave, lane, lo, blk_next, lbase);
     const int k0 = t * kPfKeys;
-    if (hvalid && k0 <= lim_hi)
-      compute_tile<D>(w, kslot(t), vslot(t), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
+    compute_tile<D>(w, kslot(t), vslot(t), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
   }
+#pragma unroll 1
+  for (; t < n_tiles; ++t) tile_sync_and_issue<D>(sv, t, n_tiles, wave, lane, lo, blk_next, lbase);
 
   if (!hvalid || row >= lq) return;
   const float lt = w.lsum[0];  // the sum over all keys of this lane's row

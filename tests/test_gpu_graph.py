@@ -1,0 +1,90 @@
+"""Captured decode steps (store + decode replayed from HIP graphs per batch bucket).
+
+Every replay is checked against the same step run eagerly through the C ABI
+(bitwise: same kernels, same launch shapes) and the first against the fp64
+oracle; eager work and synchronisations run between replays.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import paged_kv_cache_419_amd as pkv
+from paged_kv_cache_419_amd.graph import DecodeGraphs
+import workload as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _eager(w, t, out_rows, split):
+    pkv.store_kvcache(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+    pkv.paged_decode_attention(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                               t["context_lens"], w.block_size, out_rows, w.scale, split)
+    return out
+
+
+@pytest.mark.parametrize("split", [0, 32])
+def test_graph_replays_match_eager(split):
+    _note(f"graph replays, split {split}")
+    w = W.decode([1, 17, 33, 64, 5, 90, 16], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                 block_size=16, seed=21, name="graph_b7")
+    max_ctx = 96  # captured bound: every context here is shorter, and the table spans it
+    tg = w.materialize("cuda")
+    graphs = DecodeGraphs(tg["k_cache"], tg["v_cache"], w.num_q_heads, w.block_size,
+                          w.max_blocks_per_seq, max_ctx, w.scale, buckets=(1, 2, 4, 8),
+                          split_tokens=split)
+    steps = [list(range(7)), [1, 3, 5], [6], list(range(7))]
+    for i, seqs in enumerate(steps):
+        sub = w if len(seqs) == w.num_seqs else None
+        te = w.materialize("cuda")  # fresh eager copy of the same cache image
+        if sub is None:
+            idx = torch.tensor(seqs, device="cuda")
+            tin = {k: (te[k][idx] if k in ("q", "k_new", "v_new", "slot_mapping", "block_tables",
+                                            "context_lens") else te[k]) for k in te}
+        else:
+            tin = te
+        if i == 3:  # a different query for the same sequences: sign-flipped bf16
+            tin["q"] = (tin["q"].view(torch.int16) ^ torch.tensor(-32768, dtype=torch.int16,
+                                                                    device="cuda")).view(torch.bfloat16)
+        ref = _eager(w, tin, max_ctx, split)
+        got = graphs.run(tin["q"], tin["k_new"], tin["v_new"], tin["slot_mapping"],
+                         tin["block_tables"], tin["context_lens"]).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"step {i}"
+        assert torch.equal(tg["k_cache"].view(torch.int16)[tin["slot_mapping"].long()],
+                           tin["k_new"].view(torch.int16))
+        # eager work between replays
+        _ = (tin["q"].float() * 2).sum().item()
+        torch.cuda.synchronize()
+    # the first step against the fp64 oracle
+    got = graphs.run(tg["q"], tg["k_new"], tg["v_new"], tg["slot_mapping"], tg["block_tables"],
+                     tg["context_lens"]).clone()
+    torch.cuda.synchronize()
+    H.check_against_oracle(w, got, list(range(w.num_seqs)))
+
+
+def test_graph_bucket_choice_and_padding():
+    w = W.make("decode_edge_b4")
+    t = w.materialize("cuda")
+    graphs = DecodeGraphs(t["k_cache"], t["v_cache"], w.num_q_heads, w.block_size,
+                          w.max_blocks_per_seq, w.max_context_len, w.scale, buckets=(2, 8))
+    assert graphs.bucket_for(1) == 2 and graphs.bucket_for(3) == 8
+    with pytest.raises(ValueError):
+        graphs.bucket_for(9)
+    before = t["k_cache"].clone()
+    out = graphs.run(t["q"], t["k_new"], t["v_new"], t["slot_mapping"], t["block_tables"],
+                     t["context_lens"]).clone()
+    torch.cuda.synchronize()
+    # only the four new tokens' slots changed (padding rows stored nothing)
+    changed = (t["k_cache"].view(torch.int16) != before.view(torch.int16)).any(dim=(1, 2))
+    slots = np.sort(w.slot_mapping[w.slot_mapping >= 0])
+    assert np.array_equal(np.nonzero(changed.cpu().numpy())[0], slots)
+    H.check_against_oracle(w, out, list(range(w.num_seqs)))
