@@ -111,6 +111,31 @@ __device__ __forceinline__ u32x4 buffer_load16(buffer_rsrc r, uint32_t byte_off)
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0));
 }
 
+// The same descriptor as four scalar words, for inline asm.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t num_bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32) & 0xFFFFu, num_bytes,
+               static_cast<uint32_t>(kRsrcWord3)};
+}
+
+// Direct-to-LDS 16-byte load through a raw buffer descriptor: lane i's 16
+// bytes at byte voff + soff of the buffer go to LDS `dst` + 16 i (`dst` the
+// same for the whole wave).  Dwords past the descriptor's num_records (soff
+// included in the check) fetch nothing and write zeros.  Issued from inline
+// asm, like lds_dma16, so the compiler adds no waits; M0 is saved and restored.
+__device__ __forceinline__ void lds_dma16_buf(u32x4 desc, uint32_t voff, uint32_t soff, lds_bytes dst) {
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(desc), "s"(soff), "s"(lds_addr)
+      : "memory");
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

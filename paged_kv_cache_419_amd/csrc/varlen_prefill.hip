@@ -79,9 +79,7 @@ struct SeqView {
 
 // Each wave loads rows 16 * wave .. 16 * wave + 15 of every K and V tile.
 // Those 16 rows lie in one cache block (blocks hold >= 16 tokens and the rows
-// start at a multiple of 16), so one block-table entry addresses them; rows
-// past Lk are redirected to key Lk - 1, which then lies in that same block or
-// is the only key loaded.
+// start at a multiple of 16), so one block-table entry addresses them.
 constexpr int kPfWaveRows = kPfKeys / kPfWaves;
 
 // Block-table entry of this wave's rows of the tile starting at key k0 (a
@@ -92,63 +90,79 @@ __device__ __forceinline__ int64_t tile_block(const SeqView& sv, int k0, int wav
 
 // Per-lane byte offsets, inside a block, of this wave's direct-to-LDS loads of
 // one tile, relative to the wave's first row: lane (row rr = lane / CH of
-// load e, LDS position p = lane % CH) reads the chunk stored at p.
+// load e, LDS position p = lane % CH) reads the chunk stored at p.  Only the
+// offsets of load 0 are kept: load e reads rows e * RPL further on, and its
+// K swizzle differs from load 0's by 4e in the chunk index (the row bits the
+// swizzle takes from e sit above those it takes from the lane), i.e. by
+// 64 e in the byte offset; the V swizzle does not depend on e.
 template <int D>
 struct TileLoadOffsets {
-  uint32_t k[PrefillShape<D>::LOADS];
-  uint32_t v[PrefillShape<D>::LOADS];
+  uint32_t k;
+  uint32_t v;
+  __device__ __forceinline__ uint32_t koff(int e) const { return k ^ (64u * e); }
+  __device__ __forceinline__ uint32_t voff(int) const { return v; }
 };
 
 template <int D>
 __device__ __forceinline__ TileLoadOffsets<D> tile_load_offsets(int lane, int wave, uint32_t row_bytes) {
   using S = PrefillShape<D>;
+  static_assert(S::LOADS * 4 <= S::CH, "swizzle step of load e stays inside the row");
   TileLoadOffsets<D> t;
-#pragma unroll
-  for (int e = 0; e < S::LOADS; ++e) {
-    const int rel = e * S::RPL + lane / S::CH;  // row inside the wave's 16
-    const int rr = wave * kPfWaveRows + rel;     // row inside the tile
-    const int p = lane % S::CH;
-    t.k[e] = rel * row_bytes + 16 * (p ^ kswz<D>(rr));
-    t.v[e] = rel * row_bytes + 16 * (p ^ vswz<D>(rr));
-  }
+  const int rel = lane / S::CH;             // row inside the wave's 16, load 0
+  const int rr = wave * kPfWaveRows + rel;  // row inside the tile
+  const int p = lane % S::CH;
+  t.k = rel * row_bytes + 16 * (p ^ kswz<D>(rr));
+  t.v = rel * row_bytes + 16 * (p ^ vswz<D>(rr));
   return t;
 }
 
-// Issue this wave's share of the K and V tile starting at key k0 into LDS;
-// blk is tile_block(sv, k0, wave).
+// This wave's share of one K/V tile: buffer descriptors that start at the
+// wave's first row in the cache and end after its last live row (key < Lk),
+// so the loads of rows past Lk fetch nothing and leave zeros in LDS (their
+// scores are masked, and zero V rows add nothing); with no live row, or no
+// tile to load, nothing is fetched at all.  kdst / vdst: the wave's first
+// LDS row in the slot.
+struct DmaJob {
+  u32x4 kd;
+  u32x4 vd;
+  lds_bytes kdst;
+  lds_bytes vdst;
+  uint32_t row_bytes;
+};
+
+// blk is tile_block(sv, k0, wave); live = false for "nothing to load".
 template <int D>
-__device__ __forceinline__ void issue_tile(const SeqView& sv, int64_t blk, int k0, int wave, int lane,
-                                           const TileLoadOffsets<D>& lo, lds_bytes kdst,
-                                           lds_bytes vdst) {
+__device__ __forceinline__ DmaJob dma_job(const SeqView& sv, int64_t blk, int k0, int wave, bool live,
+                                          lds_bytes kdst, lds_bytes vdst) {
   using S = PrefillShape<D>;
-  const int bmask = (1 << sv.shift) - 1;
-  const int r0 = k0 + wave * kPfWaveRows;  // first key of this wave's rows
-  if (r0 + kPfWaveRows <= sv.lk) {
-    // all 16 rows live: scalar base plus the constant per-lane offsets
-    const int64_t base = ((blk << sv.shift) + (r0 & bmask)) * static_cast<int64_t>(sv.row_bytes);
-    const char* kb = reinterpret_cast<const char*>(sv.kc) + base;
-    const char* vb = reinterpret_cast<const char*>(sv.vc) + base;
-#pragma unroll
-    for (int e = 0; e < S::LOADS; ++e) {
-      const int rr0 = wave * kPfWaveRows + e * S::RPL;
-      lds_dma16(kb + lo.k[e], kdst + rr0 * S::ROWB);
-      lds_dma16(vb + lo.v[e], vdst + rr0 * S::ROWB);
-    }
+  const int r0 = k0 + wave * kPfWaveRows;
+  const int nlive = live ? max(0, min(kPfWaveRows, sv.lk - r0)) : 0;
+  const uint32_t nbytes = nlive > 0 ? (nlive - 1) * sv.row_bytes + S::ROWB : 0;
+  const int64_t base =
+      ((blk << sv.shift) + (r0 & ((1 << sv.shift) - 1))) * static_cast<int64_t>(sv.row_bytes);
+  const char* kb = reinterpret_cast<const char*>(sv.kc) + (nlive > 0 ? base : 0);
+  const char* vb = reinterpret_cast<const char*>(sv.vc) + (nlive > 0 ? base : 0);
+  return DmaJob{rsrc_words(kb, nbytes), rsrc_words(vb, nbytes), kdst + wave * kPfWaveRows * S::ROWB,
+                vdst + wave * kPfWaveRows * S::ROWB, sv.row_bytes};
+}
+
+// Load j of a DmaJob: the K loads first, then the V loads.
+template <int D>
+__device__ __forceinline__ void dma_one(const DmaJob& job, const TileLoadOffsets<D>& lo, int j) {
+  using S = PrefillShape<D>;
+  const int e = j % S::LOADS;
+  const uint32_t step = static_cast<uint32_t>(e * S::RPL) * job.row_bytes;
+  if (j < S::LOADS) {
+    lds_dma16_buf(job.kd, lo.koff(e), step, job.kdst + e * S::RPL * S::ROWB);
   } else {
-    const int64_t base = (blk << sv.shift) * static_cast<int64_t>(sv.row_bytes);
-#pragma unroll
-    for (int e = 0; e < S::LOADS; ++e) {
-      const int rr0 = wave * kPfWaveRows + e * S::RPL;  // first row of this load
-      const int rr = rr0 + lane / S::CH;
-      const int p = lane % S::CH;
-      const int kcl = min(k0 + rr, sv.lk - 1);
-      const uint32_t roff = static_cast<uint32_t>(kcl & bmask) * sv.row_bytes;
-      const char* ksrc = reinterpret_cast<const char*>(sv.kc) + base + roff + 16 * (p ^ kswz<D>(rr));
-      const char* vsrc = reinterpret_cast<const char*>(sv.vc) + base + roff + 16 * (p ^ vswz<D>(rr));
-      lds_dma16(ksrc, kdst + rr0 * S::ROWB);
-      lds_dma16(vsrc, vdst + rr0 * S::ROWB);
-    }
+    lds_dma16_buf(job.vd, lo.voff(e), step, job.vdst + e * S::RPL * S::ROWB);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void dma_all(const DmaJob& job, const TileLoadOffsets<D>& lo) {
+#pragma unroll
+  for (int j = 0; j < 2 * PrefillShape<D>::LOADS; ++j) dma_one<D>(job, lo, j);
 }
 
 template <int D>
@@ -221,13 +235,19 @@ __device__ __forceinline__ bool weights_overflow(const u32x4 (&pb)[kPfU]) {
 }
 
 // One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// The next tile's loads (job) go out one after every kGap MFMAs of the S
+// product, so the waves of a CU do not all queue their loads on the memory
+// pipeline at once right after the barrier.
 template <int D>
 __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_bytes vt,
                                              const uint32_t (&kaddr)[PrefillShape<D>::KS],
                                              const uint32_t (&vaddr)[PrefillShape<D>::DC],
                                              int k0, int lim, bool need_mask, int h,
-                                             float c) {
+                                             float c, const DmaJob& job,
+                                             const TileLoadOffsets<D>& lo) {
   using S = PrefillShape<D>;
+  constexpr int kGap = kPfKB * S::KS / (2 * S::LOADS);
+  static_assert(kGap >= 1 && kGap * 2 * S::LOADS == kPfKB * S::KS, "loads per MFMA slot");
   f32x16 s[kPfKB];
 #pragma unroll
   for (int kb = 0; kb < kPfKB; ++kb) {
@@ -236,6 +256,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
     for (int ks = 0; ks < S::KS; ++ks) {
       const u32x4 a = *(const lds_u32x4*)(kt + kaddr[ks] + kb * 32 * S::ROWB);
       s[kb] = mfma32x32x16(a, w.qb[ks], s[kb]);
+      const int i = kb * S::KS + ks;
+      if (i % kGap == kGap - 1) dma_one<D>(job, lo, i / kGap);
     }
   }
   // Keep several K operand reads in flight ahead of the MFMAs (LDS latency is
@@ -311,19 +333,24 @@ __device__ __forceinline__ lds_bytes vslot_of(lds_bytes lbase, int t) {
 }
 
 template <int D>
-__device__ __forceinline__ void tile_sync_and_issue(const SeqView& sv, int t, int n_tiles, int wave,
-                                                    int lane, const TileLoadOffsets<D>& lo,
-                                                    int64_t& blk_next, lds_bytes lbase) {
+__device__ __forceinline__ void tile_sync(int t, int n_tiles) {
   using S = PrefillShape<D>;
   switch (min(n_tiles - 1 - t, kPfStages - 2)) {  // tiles younger than t in flight
     case 2: barrier_after_loads<2 * 2 * S::LOADS>(); break;
     case 1: barrier_after_loads<1 * 2 * S::LOADS>(); break;
     default: barrier_after_loads<0>(); break;
   }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_sync_and_issue(const SeqView& sv, int t, int n_tiles, int wave,
+                                                    const TileLoadOffsets<D>& lo,
+                                                    int64_t& blk_next, lds_bytes lbase) {
+  tile_sync<D>(t, n_tiles);
   const int tn = t + kPfStages - 1;
   if (tn < n_tiles) {
-    issue_tile<D>(sv, blk_next, tn * kPfKeys, wave, lane, lo, kslot_of<D>(lbase, tn),
-                  vslot_of<D>(lbase, tn));
+    dma_all<D>(dma_job<D>(sv, blk_next, tn * kPfKeys, wave, true, kslot_of<D>(lbase, tn),
+                          vslot_of<D>(lbase, tn)), lo);
     if (tn + 1 < n_tiles) blk_next = tile_block(sv, (tn + 1) * kPfKeys, wave);
   }
 }
@@ -379,7 +406,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
   const int n_tiles = (kend + kPfKeys - 1) / kPfKeys;
   const TileLoadOffsets<D> lo = tile_load_offsets<D>(lane, wave, sv.row_bytes);
   for (int t = 0; t < min(n_tiles, kPfStages - 1); ++t)
-    issue_tile<D>(sv, tile_block(sv, t * kPfKeys, wave), t * kPfKeys, wave, lane, lo, kslot(t), vslot(t));
+    dma_all<D>(dma_job<D>(sv, tile_block(sv, t * kPfKeys, wave), t * kPfKeys, wave, true, kslot(t), vslot(t)),
+               lo);
   // block of the next tile to issue, looked up one tile ahead
   int64_t blk_next = n_tiles >= kPfStages ? tile_block(sv, (kPfStages - 1) * kPfKeys, wave) : 0;
 
@@ -443,12 +471,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
   int t = 0;
 #pragma unroll 1
   for (; t < n_compute; ++t) {
-    tile_sync_and_issue<D>(sv, t, n_tiles, wave, lane, lo, blk_next, lbase);
+    tile_sync<D>(t, n_tiles);
     const int k0 = t * kPfKeys;
-    compute_tile<D>(w, kslot(t), vslot(t), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c);
+    const bool need_mask = k0 + kPfKeys - 1 > lim_lo;
+    const int tn = t + kPfStages - 1;
+    // The next tile's loads ride along with this tile's MFMAs (with no next
+    // tile they fetch nothing and zero the slot tile t - 1 has just freed).
+    const DmaJob job = dma_job<D>(sv, blk_next, tn * kPfKeys, wave, tn < n_tiles, kslot(tn), vslot(tn));
+    if (tn + 1 < n_tiles) blk_next = tile_block(sv, (tn + 1) * kPfKeys, wave);
+    compute_tile<D>(w, kslot(t), vslot(t), kaddr, vaddr, k0, lim, need_mask, h, c, job, lo);
   }
 #pragma unroll 1
-  for (; t < n_tiles; ++t) tile_sync_and_issue<D>(sv, t, n_tiles, wave, lane, lo, blk_next, lbase);
+  for (; t < n_tiles; ++t) tile_sync_and_issue<D>(sv, t, n_tiles, wave, lo, blk_next, lbase);
+  // The last computing tile may have left zero-filling loads in flight: they
+  // must land before the workgroup's LDS is released.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (!hvalid || row >= lq) return;
   const float lt = w.lsum[0];  // the sum over all keys of this lane's row
