@@ -87,7 +87,7 @@ def kernel_sources_sha(call: str) -> str:
 # Kernels that make up one call of each boundary entry point (rocprofv3 names).
 CALL_KERNELS = {
     "paged_decode_attention": ("paged_decode_kernel", "paged_decode_combine_kernel"),
-    "varlen_prefill_attention": ("varlen_prefill_kernel",),
+    "varlen_prefill_attention": ("varlen_prefill_kernel", "prefill_plan_kernel"),
     "store_kvcache": ("store_kvcache_kernel",),
 }
 COPY_PROBE_BYTES = 1 << 30  # plain device-to-device copy that calibrates the counters
@@ -259,8 +259,10 @@ def main():
     copies = [w.materialize(dev) for _ in range(reps)]
     outs = [torch.empty_like(c["q"]) for c in copies]
     split = args.split_tokens
-    ws_bytes = pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
-                                          w.max_context_len, split) if decode else 0
+    ws_bytes = (pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                           w.max_context_len, split) if decode else
+                pkv.prefill_workspace_bytes(w.num_seqs, int(w.lq.sum()), w.num_q_heads,
+                                            w.num_kv_heads))
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     max_q = int(w.lq.max())
     max_k = int(w.lk.max())
@@ -276,7 +278,7 @@ def main():
         else:
             pkv.varlen_prefill_attention(out, c["q"], c["k_cache"], c["v_cache"], c["cu_seqlens_q"],
                                          c["cu_seqlens_k"], c["block_tables"], max_q, max_k,
-                                         w.block_size, w.scale, w.causal)
+                                         w.block_size, w.scale, w.causal, workspace)
 
     for i in range(args.warmup):
         store(copies[i % reps])

@@ -135,6 +135,15 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace pkv_varlen_prefill_attention needs for these
+ * sizes (its work list: one 64-byte record per (sequence, query tile) pair
+ * and the work-queue counters).  0 when there is nothing to do; SIZE_MAX for
+ * invalid sizes.
+ */
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                   int32_t num_kv_heads);
+
+/*
  * Variable-length prefill attention over packed sequences.  Sequence i owns
  * query rows cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 (Lq_i of them) and key
  * positions 0 .. Lk_i-1, Lk_i = cu_seqlens_k[i+1] - cu_seqlens_k[i], read from
@@ -156,6 +165,10 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
  *   block_tables  device int32 [num_seqs, max_blocks_per_seq]
  *   max_seqlen_q, max_seqlen_k   host-side bounds on Lq_i and Lk_i (size the
  *                 launch; max_seqlen_k <= max_blocks_per_seq * block_size)
+ *   workspace     device buffer of at least pkv_prefill_workspace_bytes(...)
+ *                 bytes, 16-byte aligned; rewritten by every call (calls that
+ *                 share one workspace must not overlap in time), contents
+ *                 undefined afterwards.
  * num_seqs == 0 or total_q == 0 is a no-op.
  */
 pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_cache,
@@ -166,7 +179,8 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
                                         int32_t max_seqlen_k, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t block_size, int32_t max_blocks_per_seq,
-                                        float scale, int32_t causal, void* stream);
+                                        float scale, int32_t causal, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* pkv_last_error(void);

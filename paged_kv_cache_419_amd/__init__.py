@@ -7,5 +7,6 @@ tensors into the C calls.
 """
 from .binding import (  # noqa: F401
     EXPORTS, LIB_PATH, PagedKVError, decode_split_tokens, decode_workspace_bytes, load,
-    paged_decode_attention, store_kvcache, varlen_prefill_attention, version,
+    paged_decode_attention, prefill_workspace_bytes, store_kvcache, varlen_prefill_attention,
+    version,
 )

@@ -24,6 +24,7 @@ EXPORTS = (
     "pkv_decode_workspace_bytes",
     "pkv_decode_split_tokens",
     "pkv_paged_decode_attention",
+    "pkv_prefill_workspace_bytes",
     "pkv_varlen_prefill_attention",
     "pkv_last_error",
     "pkv_version",
@@ -58,8 +59,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pkv_paged_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                i32, i32, f32, i32, vp, sz, vp]
     lib.pkv_paged_decode_attention.restype = ctypes.c_int
+    lib.pkv_prefill_workspace_bytes.argtypes = [i32, i64, i32, i32]
+    lib.pkv_prefill_workspace_bytes.restype = sz
     lib.pkv_varlen_prefill_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
-                                                 i32, i32, i32, i32, i32, f32, i32, vp]
+                                                 i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.pkv_varlen_prefill_attention.restype = ctypes.c_int
     lib.pkv_last_error.argtypes = []
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -154,12 +157,23 @@ def paged_decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
         float(scale), split_tokens, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def prefill_workspace_bytes(num_seqs: int, total_q: int, num_q_heads: int,
+                            num_kv_heads: int) -> int:
+    r = load().pkv_prefill_workspace_bytes(num_seqs, total_q, num_q_heads, num_kv_heads)
+    if r == ctypes.c_size_t(-1).value:
+        raise PagedKVError(PKV_ERR_INVALID_ARG, "invalid sizes for the prefill workspace")
+    return int(r)
+
+
 def varlen_prefill_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                              v_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
                              cu_seqlens_k: torch.Tensor, block_tables: torch.Tensor,
                              max_seqlen_q: int, max_seqlen_k: int, block_size: int,
-                             scale: float, causal: bool = True, stream=None) -> None:
-    """Causal (or full) attention of packed query rows over their cached keys."""
+                             scale: float, causal: bool = True,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Causal (or full) attention of packed query rows over their cached keys.
+
+    ``workspace`` (uint8, on the device) is allocated per call when not given."""
     for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _need(t, torch.bfloat16, name, 3)
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
@@ -171,7 +185,12 @@ def varlen_prefill_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.
     if out.shape != q.shape or k_cache.shape[2] != d or v_cache.shape != k_cache.shape \
             or cu_seqlens_k.shape[0] != ns + 1 or block_tables.shape[0] != ns:
         raise ValueError("varlen_prefill_attention: inconsistent shapes")
+    need = prefill_workspace_bytes(ns, total_q, hq, hkv) if hkv > 0 and hq % hkv == 0 else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().pkv_varlen_prefill_attention(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
         _ptr(block_tables), ns, total_q, max_seqlen_q, max_seqlen_k, hq, hkv, d, block_size,
-        block_tables.shape[1], float(scale), 1 if causal else 0, _stream(stream)))
+        block_tables.shape[1], float(scale), 1 if causal else 0, _ptr(workspace), ws_bytes,
+        _stream(stream)))

@@ -34,6 +34,9 @@ def hipcc() -> str:
 def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # A queue slot taken by one lane is used much later; the wave-level
+            # atomic rewrite would wait for the atomic's return right away.
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -196,6 +196,15 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
                     "paged_decode_attention launch");
 }
 
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int64_t total_q, int32_t num_q_heads,
+                                   int32_t num_kv_heads) {
+  if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads)
+    return SIZE_MAX;
+  if (num_seqs == 0 || total_q == 0) return 0;
+  return pkv::prefill_workspace_bytes(num_seqs, total_q, num_q_heads / num_kv_heads);
+}
+
 pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_cache,
                                         const void* v_cache, const int32_t* cu_seqlens_q,
                                         const int32_t* cu_seqlens_k,
@@ -204,7 +213,8 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
                                         int32_t max_seqlen_k, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t block_size, int32_t max_blocks_per_seq,
-                                        float scale, int32_t causal, void* stream) {
+                                        float scale, int32_t causal, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(PKV_ERR_INVALID_ARG, "negative size argument");
   pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -224,6 +234,17 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
     return fail(PKV_ERR_INVALID_ARG, "bf16 buffers must be 16-byte aligned");
   if (total_q > (int64_t{1} << 31) - 1)
     return fail(PKV_ERR_UNSUPPORTED, "total_q beyond 2^31 - 1 rows");
+  // output rows of one sequence and head are addressed with 32-bit offsets
+  if (static_cast<int64_t>(max_seqlen_q) * num_q_heads * head_dim * 2 > (int64_t{1} << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "max_seqlen_q * num_q_heads * head_dim beyond 2^30");
+  // work items (pairs x kv heads x head groups) are counted in 32 bits
+  if ((total_q / 32 + num_seqs + 1) * static_cast<int64_t>(num_q_heads) > (int64_t{1} << 30))
+    return fail(PKV_ERR_UNSUPPORTED, "too many prefill work items");
+  const size_t need = pkv_prefill_workspace_bytes(num_seqs, total_q, num_q_heads, num_kv_heads);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? size_t{0} : workspace_bytes);
+  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
   pkv::PrefillArgs a{};
   a.out = out;
@@ -243,7 +264,8 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
   a.max_seqlen_q = max_seqlen_q;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(pkv::launch_varlen_prefill(a, static_cast<hipStream_t>(stream)),
+  a.total_q = total_q;
+  return hip_status(pkv::launch_varlen_prefill(a, workspace, static_cast<hipStream_t>(stream)),
                     "varlen_prefill_attention launch");
 }
 

@@ -68,6 +68,19 @@ __device__ __forceinline__ void lds_dma16(const void* src, lds_bytes dst) {
       : "memory");
 }
 
+// The same barrier, written so the compiler sees the wait: it then knows that
+// every vector-memory access it issued before, except the youngest N, has
+// completed, and adds no waits of its own for them later.  The empty asm
+// statements keep memory accesses from moving across.
+template <int N>
+__device__ __forceinline__ void barrier_after_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));  // vmcnt(N) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier once at most N vector-memory loads of this wave are still
 // outstanding (direct-to-LDS loads included) and its LDS accesses are done:
 // this wave's older loads have landed, younger ones stay in flight.  One asm statement with a memory

@@ -50,8 +50,12 @@ struct PrefillArgs {
   int32_t max_seqlen_q;
   int32_t causal;
   float scale_log2;
+  int64_t total_q;
 };
 
-hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream);
+// Workspace of the prefill launch: work queues and the list of (sequence,
+// q tile) pairs, at most ceil(total_q / rows per workgroup) + num_seqs of them.
+size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_q, int32_t group);
+hipError_t launch_varlen_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace pkv

@@ -243,7 +243,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
                                              const uint32_t (&kaddr)[PrefillShape<D>::KS],
                                              const uint32_t (&vaddr)[PrefillShape<D>::DC],
                                              int k0, int lim, bool need_mask, int h,
-                                             float c, const DmaJob& job,
+                                             float c, float sgn, const DmaJob& job,
                                              const TileLoadOffsets<D>& lo) {
   using S = PrefillShape<D>;
   constexpr int kGap = kPfKB * S::KS / (2 * S::LOADS);
@@ -269,7 +269,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
     for (int kb = 0; kb < kPfKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        if (k0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3) > lim) s[kb][v] = -INFINITY;
+        if (k0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3) > lim) s[kb][v] = -INFINITY * sgn;
   }
   // Weights p = exp2(s c - m) against the running reference m.  m only has
   // to bound the scores loosely: the weights are consistent with the sums and
@@ -277,25 +277,27 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
   // the max is not computed at all: the tile's weights are checked instead,
   // and only when some weight reaches 2^kRescaleSlack (its row's max rose by
   // that much, rare after the first tiles) is m raised and O rescaled.
+  // c may be negative (sgn = -1): masked scores are then +inf, and the
+  // largest s c of a row is |c| times the largest s sgn.
   if (__ballot(w.m == -INFINITY) != 0) {  // first tile of this wave
-    float mx = s[0][0];
+    float mx = s[0][0] * sgn;
 #pragma unroll
     for (int kb = 0; kb < kPfKB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v] * sgn);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    w.m = mx * c;
+    w.m = mx * (c * sgn);
   }
   u32x4 pb[kPfU];
   tile_weights(s, pb, w.m, c);
   if (__ballot(weights_overflow(pb)) != 0) {
-    float mx = s[0][0];
+    float mx = s[0][0] * sgn;
 #pragma unroll
     for (int kb = 0; kb < kPfKB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v] * sgn);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(w.m, mx * c);
+    const float m_new = fmaxf(w.m, mx * (c * sgn));
     const float alpha = fast_exp2(w.m - m_new);
     w.lsum *= alpha;
 #pragma unroll
@@ -355,92 +357,201 @@ __device__ __forceinline__ void tile_sync_and_issue(const SeqView& sv, int t, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Work list and persistent workgroups.
+//
+// A work item is (sequence, q tile, kv head, head group).  A small plan
+// kernel lists the (sequence, q tile) pairs that hold at least one query row,
+// sequence by sequence and latest q tile first, as records carrying what a
+// workgroup needs to start on the pair; item i is pair i / ipp, kv head
+// (i % ipp) / head_groups, head group i % head_groups (ipp = Hkv *
+// head_groups).  Items are dealt to eight queues, item i to queue i % 8, one
+// queue per XCD: a workgroup takes items from the queue of the XCD it runs on
+// (its hardware XCC id), so with 8 | Hkv each XCD serves one kv head and the
+// K/V it streams stay in its own L2.  A queue is a counter in the workspace
+// bumped by one atomic per item; once its own queue is drained a workgroup
+// takes items from the others.
+//
+// Exactly two workgroups per CU are launched, and each runs items back to
+// back, so no workgroup waits on the hardware dispatcher, and the start of the
+// next item overlaps the end of the current one: its record and its queue
+// slot are fetched when the current item starts, its Q rows and its first K/V
+// tile are loaded during the current item's last tile.  The LDS ring of K/V
+// tiles simply runs on from one item into the next.
+
+constexpr int kQueues = 8;        // one per XCD
+constexpr int kQueueStride = 32;  // ints between queue counters (one 128-byte line each)
+constexpr int kRecInts = 16;      // ints per pair record
+constexpr int kWsCountersInts = kQueues * kQueueStride;
+constexpr int kWsNPairsInt = kWsCountersInts;          // int index of the pair count
+constexpr int kWsRecsInt = kWsCountersInts + 16;       // first record (64-byte aligned)
+constexpr uint32_t kXccIdReg = (31u << 11) | 20u;      // s_getreg: HW_REG_XCC_ID, 32 bits
+
+// Record of one (sequence, q tile) pair: sequence, q tile, first query row,
+// Lq, Lk, and the block-table entry of tile 0's rows for waves 0..3.
+enum : int { kRecSeq = 0, kRecQtile, kRecQstart, kRecLq, kRecLk, kRecBlk0 };
+
+struct PrefillSched {
+  int* ws;               // workspace: queue counters, pair count, pair records
+  int32_t heads_per_wg;  // query heads of one kv head per workgroup
+  int32_t head_groups;   // group / heads_per_wg
+  int32_t rows_per_wg;   // query rows per workgroup
+};
+
+// Entry of block table row `seq` holding key position k (clamped to the row,
+// so the read stays inside the table whatever the sequence's length).
+__device__ __forceinline__ int32_t block_entry(const PrefillArgs& a, int seq, int k) {
+  return a.block_tables[static_cast<int64_t>(seq) * a.max_blocks_per_seq +
+                        min(k >> a.block_shift, a.max_blocks_per_seq - 1)];
+}
+
+// Lists the pairs into the workspace (at most `cap` of them: the bound the
+// workspace was sized for, which holds when cu_seqlens_q ends at total_q) and
+// clears the queue counters.
+__global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32_t rows_per_wg,
+                                                            int32_t cap, int* ws) {
+  __shared__ int s_incl[1024];
+  __shared__ int s_total;
+  const int tid = threadIdx.x;
+  if (tid < kWsCountersInts) ws[tid] = 0;
+  if (tid == 0) s_total = 0;
+  __syncthreads();
+  for (int s0 = 0; s0 < a.num_seqs; s0 += 1024) {
+    const int s = s0 + tid;
+    const int lq = s < a.num_seqs ? a.cu_q[s + 1] - a.cu_q[s] : 0;
+    const int nqt = lq > 0 ? (lq + rows_per_wg - 1) / rows_per_wg : 0;
+    s_incl[tid] = nqt;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan of the pair counts
+      const int v = tid >= d ? s_incl[tid - d] : 0;
+      __syncthreads();
+      s_incl[tid] += v;
+      __syncthreads();
+    }
+    const int base = s_total;
+    const int chunk = s_incl[1023];
+    // one record per pair of this chunk of sequences, all threads together
+    for (int r = tid; r < min(chunk, cap - base); r += 1024) {
+      int lo = 0, hi = 1023;  // first thread whose inclusive count exceeds r
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_incl[mid] > r) hi = mid; else lo = mid + 1;
+      }
+      const int seq = s0 + lo;
+      const int first = s_incl[lo] - (lo > 0 ? s_incl[lo - 1] : 0);  // pairs of seq
+      const int rank = r - (s_incl[lo] - first);
+      const int q_start = a.cu_q[seq];
+      const int slq = a.cu_q[seq + 1] - q_start;
+      int4* rec = reinterpret_cast<int4*>(ws + kWsRecsInt + static_cast<int64_t>(base + r) * kRecInts);
+      rec[0] = int4{seq, first - 1 - rank, q_start, slq};
+      rec[1] = int4{a.cu_k[seq + 1] - a.cu_k[seq], block_entry(a, seq, 0 * kPfWaveRows),
+                    block_entry(a, seq, 1 * kPfWaveRows), block_entry(a, seq, 2 * kPfWaveRows)};
+      rec[2] = int4{block_entry(a, seq, 3 * kPfWaveRows), 0, 0, 0};
+    }
+    __syncthreads();
+    if (tid == 0) s_total = base + chunk;
+    __syncthreads();
+  }
+  if (tid == 0) ws[kWsNPairsInt] = min(s_total, cap);
+}
+
+__device__ __forceinline__ int queue_size(int n_items, int q) {
+  return n_items > q ? (n_items - q + kQueues - 1) / kQueues : 0;
+}
+
+// Item for slot `ticket` already taken in queue q0 (ticket < 0: none taken);
+// when q0 is drained, takes an item from another queue.  -1 when all are.
+__device__ int claim_item(int* counters, int n_items, int q0, int ticket) {
+  if (ticket >= 0 && ticket < queue_size(n_items, q0)) return ticket * kQueues + q0;
+  for (int k = 1; k < kQueues; ++k) {
+    const int q = (q0 + k) & (kQueues - 1);
+    const int size = queue_size(n_items, q);
+    if (__atomic_load_n(&counters[q * kQueueStride], __ATOMIC_RELAXED) >= size) continue;
+    const int j = atomicAdd(&counters[q * kQueueStride], 1);
+    if (j < size) return j * kQueues + q;
+  }
+  return -1;
+}
+
+// One work item as seen by one wave (wave-uniform values).
+struct Item {
+  int seq, qtile, q_start, lq, lk, g, hg;
+  int64_t blk0;  // block of this wave's rows of tile 0
+};
+
+// Every lane reads the same record (one request per wave), then the fields
+// are made wave-uniform.
+__device__ __forceinline__ void load_record(const int* ws, int pair, u32x4 (&r)[3]) {
+  const int* p = ws + kWsRecsInt + static_cast<int64_t>(pair) * kRecInts;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) r[i] = ldg16(p + 4 * i);
+}
+
+__device__ __forceinline__ Item item_of(const PrefillSched& sc, int id, const u32x4 (&r)[3], int wave,
+                                        int ipp) {
+  Item it;
+  const int rem = id % ipp;
+  it.g = rem / sc.head_groups;
+  it.hg = rem % sc.head_groups;
+  auto f = [&](int i) { return __builtin_amdgcn_readfirstlane(static_cast<int>(r[i >> 2][i & 3])); };
+  it.seq = f(kRecSeq);
+  it.qtile = f(kRecQtile);
+  it.q_start = f(kRecQstart);
+  it.lq = f(kRecLq);
+  it.lk = f(kRecLk);
+  const int b = wave == 0 ? f(kRecBlk0) : wave == 1 ? f(kRecBlk0 + 1) : wave == 2 ? f(kRecBlk0 + 2)
+                                                                                   : f(kRecBlk0 + 3);
+  it.blk0 = b;
+  return it;
+}
+
 template <int D>
-__global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
-    PrefillArgs a, int32_t heads_per_wg, int32_t head_groups, int32_t rows_per_wg,
-    int32_t q_tiles) {
+__device__ __forceinline__ SeqView seq_view(const PrefillArgs& a, const Item& it) {
+  SeqView sv;
+  sv.row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+  sv.kc = static_cast<const uint16_t*>(a.k_cache) + static_cast<int64_t>(it.g) * D;
+  sv.vc = static_cast<const uint16_t*>(a.v_cache) + static_cast<int64_t>(it.g) * D;
+  sv.bt = (const __attribute__((address_space(4))) int32_t*)(a.block_tables) +
+          static_cast<int64_t>(it.seq) * a.max_blocks_per_seq;
+  sv.lk = it.lk;
+  sv.shift = a.block_shift;
+  return sv;
+}
+
+// Number of K/V tiles the rows of an item's workgroup see.
+__device__ __forceinline__ int item_tiles(const PrefillArgs& a, const PrefillSched& sc, const Item& it) {
+  const int r0 = it.qtile * sc.rows_per_wg;
+  const int last_row = min(r0 + sc.rows_per_wg, it.lq) - 1;
+  const int kend = a.causal ? min(it.lk, it.lk - it.lq + last_row + 1) : it.lk;
+  return (kend + kPfKeys - 1) / kPfKeys;
+}
+
+template <int D>
+__global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillArgs a, PrefillSched sc) {
   using S = PrefillShape<D>;
+  constexpr int kStores = S::DC * 4;  // output stores per wave and item
   // kPfStages slots, each a K tile followed by a V tile
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kPfStages * 2 * S::TILE];
-
-  // item = ((seq * q_tiles + q tile rank) * Hkv + g) * head_groups + hg
-  int64_t rest = blockIdx.x;
-  const int hg = static_cast<int>(rest % head_groups);
-  rest /= head_groups;
-  const int g = static_cast<int>(rest % a.num_kv_heads);
-  rest /= a.num_kv_heads;
-  const int qtile = q_tiles - 1 - static_cast<int>(rest % q_tiles);
-  const int seq = static_cast<int>(rest / q_tiles);
-
-  const int q_start = a.cu_q[seq];
-  const int lq = a.cu_q[seq + 1] - q_start;
-  const int lk = a.cu_k[seq + 1] - a.cu_k[seq];
-  const int off = lk - lq;
-  const int r0 = qtile * rows_per_wg;
-  if (r0 >= lq) return;
+  __shared__ int s_item[4];  // ids of coming items, published through the LDS
+  const lds_bytes lbase = (lds_bytes)smem;
+  auto kslot = [&](int t) { return kslot_of<D>(lbase, t); };
+  auto vslot = [&](int t) { return vslot_of<D>(lbase, t); };
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int m32 = lane & 31;
   const int h = lane >> 5;
-  const int hl = hg * heads_per_wg + wave % heads_per_wg;
-  const bool hvalid = hl < a.group;
-  const int head = g * a.group + (hvalid ? hl : 0);
-  const int rbase = r0 + (wave / heads_per_wg) * kPfRows;
-  const int row = rbase + m32;
-
-  SeqView sv;
-  sv.row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
-  sv.kc = static_cast<const uint16_t*>(a.k_cache) + static_cast<int64_t>(g) * D;
-  sv.vc = static_cast<const uint16_t*>(a.v_cache) + static_cast<int64_t>(g) * D;
-  sv.bt = (const __attribute__((address_space(4))) int32_t*)(a.block_tables) +
-          static_cast<int64_t>(seq) * a.max_blocks_per_seq;
-  sv.lk = lk;
-  sv.shift = a.block_shift;
-  const lds_bytes lbase = (lds_bytes)smem;
-  auto kslot = [&](int t) { return kslot_of<D>(lbase, t); };
-  auto vslot = [&](int t) { return vslot_of<D>(lbase, t); };
-
-  const int last_row = min(r0 + rows_per_wg, lq) - 1;
-  const int kend = a.causal ? min(lk, off + last_row + 1) : lk;
-  const int n_tiles = (kend + kPfKeys - 1) / kPfKeys;
-  const TileLoadOffsets<D> lo = tile_load_offsets<D>(lane, wave, sv.row_bytes);
-  for (int t = 0; t < min(n_tiles, kPfStages - 1); ++t)
-    dma_all<D>(dma_job<D>(sv, tile_block(sv, t * kPfKeys, wave), t * kPfKeys, wave, true, kslot(t), vslot(t)),
-               lo);
-  // block of the next tile to issue, looked up one tile ahead
-  int64_t blk_next = n_tiles >= kPfStages ? tile_block(sv, (kPfStages - 1) * kPfKeys, wave) : 0;
-
-  WaveState<D> w;
-  // With a negative scale, negate Q (exact in bf16) and use |scale|, so the
-  // exponent scale c is positive and the row max of raw scores is the max.
-  const float c = fabsf(a.scale_log2);
-  {
-    const bool live = hvalid && row < lq;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<int64_t>(q_start + (live ? row : 0)) * a.num_q_heads + head) * D +
-                         8 * h;
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) w.qb[ks] = live ? ldg16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
-    // Q (and tile 0) must have landed before the loop: a wait the compiler
-    // sees, so it adds none inside the loop, where the only vector loads are
-    // the direct-to-LDS ones it does not track.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    if (a.scale_log2 < 0.f) {
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) w.qb[ks] ^= 0x80008000u;
-    }
-  }
-#pragma unroll
-  for (int cb = 0; cb < S::DC; ++cb) w.o[cb] = f32x16{};
-  w.m = -INFINITY;
-  w.lsum = f32x16{};
-
-  // last visible key of this lane's row (padding rows borrow the last row's)
-  const int lim = a.causal ? min(off + min(row, lq - 1), lk - 1) : lk - 1;
-  // smallest such limit over this wave's rows, and the wave's largest
-  const int lim_lo = a.causal ? min(off + min(rbase, lq - 1), lk - 1) : lk - 1;
-  const int lim_hi = a.causal ? min(off + min(rbase + kPfRows - 1, lq - 1), lk - 1) : lk - 1;
+  const int xcc = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg(kXccIdReg)) & (kQueues - 1);
+  int* counters = sc.ws;
+  const int ipp = a.num_kv_heads * sc.head_groups;
+  const int n_items = sc.ws[kWsNPairsInt] * ipp;
+  // Exponent scale of the raw scores (log2 domain).  A zero scale is taken as
+  // a tiny one: every visible key then gets weight 1, and masked keys (score
+  // -inf) still get 0.
+  const float c = a.scale_log2 != 0.f ? a.scale_log2 : 1e-30f;
+  const float sgn = c > 0.f ? 1.f : -1.f;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
+  const TileLoadOffsets<D> lo = tile_load_offsets<D>(lane, wave, row_bytes);
 
   // Per-lane LDS byte offsets of the MFMA operands inside a tile.
   uint32_t kaddr[S::KS];
@@ -459,68 +570,213 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(
     }
   }
 
-  // Tile loop over a ring of kPfStages LDS slots, one barrier per tile: each
-  // wave waits for its own loads of tile t (younger tiles stay in flight) and
-  // for its LDS reads of tile t - 1, the workgroup syncs, and only then is
-  // tile t + kPfStages - 1 issued into the slot tile t - 1 has just freed.
-  // Tiles past lim_hi hold no key any row of this wave sees (they exist for
-  // other row blocks of the workgroup); padding heads compute nothing.  The
-  // computing tiles come first, in a loop of their own, so the accumulators
-  // are updated unconditionally inside it.
-  const int n_compute = hvalid ? min(n_tiles, lim_hi / kPfKeys + 1) : 0;
-  int t = 0;
-#pragma unroll 1
-  for (; t < n_compute; ++t) {
-    tile_sync<D>(t, n_tiles);
-    const int k0 = t * kPfKeys;
-    const bool need_mask = k0 + kPfKeys - 1 > lim_lo;
-    const int tn = t + kPfStages - 1;
-    // The next tile's loads ride along with this tile's MFMAs (with no next
-    // tile they fetch nothing and zero the slot tile t - 1 has just freed).
-    const DmaJob job = dma_job<D>(sv, blk_next, tn * kPfKeys, wave, tn < n_tiles, kslot(tn), vslot(tn));
-    if (tn + 1 < n_tiles) blk_next = tile_block(sv, (tn + 1) * kPfKeys, wave);
-    compute_tile<D>(w, kslot(t), vslot(t), kaddr, vaddr, k0, lim, need_mask, h, c, job, lo);
-  }
-#pragma unroll 1
-  for (; t < n_tiles; ++t) tile_sync_and_issue<D>(sv, t, n_tiles, wave, lo, blk_next, lbase);
-  // The last computing tile may have left zero-filling loads in flight: they
-  // must land before the workgroup's LDS is released.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // This wave's query head and first row of an item, and its Q loads.
+  auto wave_head = [&](const Item& it) {
+    return it.g * a.group + it.hg * sc.heads_per_wg + wave % sc.heads_per_wg;
+  };
+  auto wave_rbase = [&](const Item& it) {
+    return it.qtile * sc.rows_per_wg + (wave / sc.heads_per_wg) * kPfRows;
+  };
+  auto load_q = [&](const Item& it, u32x4 (&dst)[S::KS]) {
+    const int row = wave_rbase(it) + m32;
+    const bool live = row < it.lq;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<int64_t>(it.q_start + (live ? row : 0)) * a.num_q_heads +
+                          wave_head(it)) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) dst[ks] = live ? ldg16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+  };
 
-  if (!hvalid || row >= lq) return;
-  const float lt = w.lsum[0];  // the sum over all keys of this lane's row
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  uint16_t* op = static_cast<uint16_t*>(a.out) +
-                 (static_cast<int64_t>(q_start + row) * a.num_q_heads + head) * D + 4 * h;
-#pragma unroll
-  for (int cb = 0; cb < S::DC; ++cb) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x16& ov = w.o[cb];
-      const uint2 v = {pack_bf16x2(ov[4 * j] * inv, ov[4 * j + 1] * inv),
-                       pack_bf16x2(ov[4 * j + 2] * inv, ov[4 * j + 3] * inv)};
-      *reinterpret_cast<uint2*>(op + 32 * cb + 8 * j) = v;
-    }
+  // Item ids go through a ring of four LDS slots: id(i) in slot i % 4.  The
+  // id of item i + 2 is claimed by thread 0 when item i starts (with the
+  // queue ticket it took during item i - 1) and read by every wave at item
+  // i's last ring step, where the record of item i + 2 is loaded; item i + 1,
+  // whose record is in registers by then, gets its Q rows and first K/V tile
+  // loaded there.
+  int ticket = -2;  // thread 0: queue slot taken for a later item (-2: the queues are drained)
+  if (threadIdx.x == 0) {
+    const int i0 = claim_item(counters, n_items, xcc, atomicAdd(&counters[xcc * kQueueStride], 1));
+    const int i1 = i0 >= 0 ? claim_item(counters, n_items, xcc, atomicAdd(&counters[xcc * kQueueStride], 1)) : -1;
+    s_item[0] = i0;
+    s_item[1] = i1;
+    ticket = i1 >= 0 ? atomicAdd(&counters[xcc * kQueueStride], 1) : -2;
   }
+  __syncthreads();
+  const int first_id = __builtin_amdgcn_readfirstlane(s_item[0]);
+  if (first_id < 0) return;
+  int nxt_id = __builtin_amdgcn_readfirstlane(s_item[1]);
+
+  Item cur;
+  WaveState<D> w;
+  u32x4 rec[3];
+  {
+    load_record(sc.ws, first_id / ipp, rec);
+    cur = item_of(sc, first_id, rec, wave, ipp);
+    dma_all<D>(dma_job<D>(seq_view<D>(a, cur), cur.blk0, 0, wave, item_tiles(a, sc, cur) > 0, kslot(0),
+                          vslot(0)), lo);
+    load_q(cur, w.qb);
+    load_record(sc.ws, max(nxt_id, 0) / ipp, rec);
+    // Once per workgroup: let everything land, so that the compiler knows no
+    // load of this start is pending when the item loop begins.
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  }
+
+  int T = 0;  // ring position of the current tile (the tiles of all items, in order)
+#pragma unroll 1
+  for (int item_no = 0;; ++item_no) {
+    if (threadIdx.x == 0)
+      s_item[(item_no + 2) & 3] = ticket == -2 ? -1 : claim_item(counters, n_items, xcc, ticket);
+
+    const SeqView sv = seq_view<D>(a, cur);
+    const int head = wave_head(cur);
+    const int rbase = wave_rbase(cur);
+    const int row = rbase + m32;
+    const int off = cur.lk - cur.lq;
+    const int n_tiles = item_tiles(a, sc, cur);
+    const int n_eff = max(n_tiles, 1);  // an item without keys still takes one (empty) ring step
+    // last visible key of this lane's row (padding rows borrow the last row's)
+    const int lim = a.causal ? min(off + min(row, cur.lq - 1), cur.lk - 1) : cur.lk - 1;
+    // smallest such limit over this wave's rows, and the wave's largest
+    const int lim_lo = a.causal ? min(off + min(rbase, cur.lq - 1), cur.lk - 1) : cur.lk - 1;
+    const int lim_hi =
+        a.causal ? min(off + min(rbase + kPfRows - 1, cur.lq - 1), cur.lk - 1) : cur.lk - 1;
+    // Tiles past lim_hi hold no key any row of this wave sees (they exist for
+    // other row blocks of the workgroup): the computing tiles come first, in
+    // a loop of their own, so the accumulators are updated unconditionally.
+    const int n_compute = min(n_tiles, lim_hi / kPfKeys + 1);
+
+#pragma unroll
+    for (int cb = 0; cb < S::DC; ++cb) w.o[cb] = f32x16{};
+    w.m = -INFINITY;
+    w.lsum = f32x16{};
+
+    // Start of ring step T (tile t of this item): wait for this wave's loads
+    // of the tile (at an item's first tile, the previous item's output stores,
+    // issued after them, may stay in flight) and for its LDS reads of the
+    // previous tile, then sync the workgroup; the slot of the previous tile
+    // is free from here on.
+    auto sync_step = [&](int t) {
+      if (t == 0 && item_no > 0) {
+        barrier_after_vm<kStores>();
+      } else {
+        barrier_after_vm<0>();
+      }
+    };
+    int64_t blk_next = n_eff > 1 ? tile_block(sv, kPfKeys, wave) : 0;
+    auto inner_step = [&](int t) -> DmaJob {  // loads of tile t + 1
+      sync_step(t);
+      const DmaJob job = dma_job<D>(sv, blk_next, (t + 1) * kPfKeys, wave, t + 1 < n_tiles, kslot(T + 1),
+                                    vslot(T + 1));
+      if (t + 2 < n_eff) blk_next = tile_block(sv, (t + 2) * kPfKeys, wave);
+      return job;
+    };
+
+    const int n_inner = n_eff - 1;
+    int t = 0;
+#pragma unroll 1
+    for (; t < min(n_compute, n_inner); ++t, ++T) {
+      const DmaJob job = inner_step(t);
+      const int k0 = t * kPfKeys;
+      compute_tile<D>(w, kslot(T), vslot(T), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c, sgn, job, lo);
+    }
+#pragma unroll 1
+    for (; t < n_inner; ++t, ++T) dma_all<D>(inner_step(t), lo);
+
+    // Last ring step of the item: the loads that follow are the next item's
+    // tile 0 (none after the last item, whose step then fetches nothing).
+    sync_step(t);
+    // Every word of the record stays allocated until here (no other value
+    // may take a register a record load still writes).
+    asm volatile("" ::"v"(rec[0]), "v"(rec[1]), "v"(rec[2]));
+    const bool has_next = nxt_id >= 0;
+    const Item nx = item_of(sc, max(nxt_id, 0), rec, wave, ipp);
+    u32x4 qn[S::KS];
+    {
+      Item nq = nx;
+      if (!has_next) nq.lq = 0;  // loads nothing
+      load_q(nq, qn);
+    }
+    const DmaJob job = dma_job<D>(seq_view<D>(a, nx), nx.blk0, 0, wave, has_next && item_tiles(a, sc, nx) > 0,
+                                  kslot(T + 1), vslot(T + 1));
+    const int after = has_next ? __builtin_amdgcn_readfirstlane(s_item[(item_no + 2) & 3]) : -1;
+    load_record(sc.ws, max(after, 0) / ipp, rec);
+    if (threadIdx.x == 0) ticket = after >= 0 ? atomicAdd(&counters[xcc * kQueueStride], 1) : -2;
+    if (t < n_compute) {
+      const int k0 = t * kPfKeys;
+      compute_tile<D>(w, kslot(T), vslot(T), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c, sgn, job, lo);
+    } else {
+      dma_all<D>(job, lo);
+    }
+    ++T;
+
+    // Output rows of this wave: buffer stores whose range ends after row Lq - 1
+    // of this head, so the padding rows' stores are dropped by the hardware
+    // (the count of store instructions stays kStores, whatever the rows).
+    {
+      const float lt = w.lsum[0];  // the sum over all keys of this lane's row
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const uint32_t hrow = static_cast<uint32_t>(a.num_q_heads) * D * 2;  // bytes per token row
+      const char* ob = static_cast<const char*>(a.out) +
+                       (static_cast<int64_t>(cur.q_start) * a.num_q_heads + head) * D * 2;
+      const buffer_rsrc orsrc = make_rsrc(ob, cur.lq > 0 ? (cur.lq - 1) * hrow + D * 2 : 0);
+      const uint32_t obase = static_cast<uint32_t>(row) * hrow + 8 * h;
+#pragma unroll
+      for (int cb = 0; cb < S::DC; ++cb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x16& ov = w.o[cb];
+          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+          const u32x2 v = {pack_bf16x2(ov[4 * j] * inv, ov[4 * j + 1] * inv),
+                           pack_bf16x2(ov[4 * j + 2] * inv, ov[4 * j + 3] * inv)};
+          __builtin_amdgcn_raw_buffer_store_b64(v, orsrc, static_cast<int>(obase + 2 * (32 * cb + 8 * j)), 0, 0);
+        }
+      }
+    }
+    if (!has_next) break;
+    cur = nx;
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) w.qb[ks] = qn[ks];
+    nxt_id = after;
+  }
+  // The last ring step's loads (zero fills) and the output stores must be
+  // done before the workgroup's LDS is released.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace
 
-hipError_t launch_varlen_prefill(const PrefillArgs& a, hipStream_t stream) {
+size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_q, int32_t group) {
+  const int32_t heads_per_wg = (group % 4 == 0) ? 4 : ((group % 2 == 0) ? 2 : 1);
+  const int64_t rows_per_wg = kPfRows * (kPfWaves / heads_per_wg);
+  const int64_t cap = (total_q + rows_per_wg - 1) / rows_per_wg + num_seqs;
+  return static_cast<size_t>(kWsRecsInt) * 4 + static_cast<size_t>(cap) * kRecInts * 4;
+}
+
+hipError_t launch_varlen_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream) {
   const int32_t heads_per_wg = (a.group % 4 == 0) ? 4 : ((a.group % 2 == 0) ? 2 : 1);
-  const int32_t head_groups = a.group / heads_per_wg;
-  const int32_t rows_per_wg = kPfRows * (kPfWaves / heads_per_wg);
-  const int32_t q_tiles = (a.max_seqlen_q + rows_per_wg - 1) / rows_per_wg;
-  const int64_t total =
-      static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * head_groups * q_tiles;
-  if (total == 0) return hipSuccess;
-  const dim3 grid(static_cast<uint32_t>(total));
+  PrefillSched sc;
+  sc.ws = static_cast<int*>(workspace);
+  sc.heads_per_wg = heads_per_wg;
+  sc.head_groups = a.group / heads_per_wg;
+  sc.rows_per_wg = kPfRows * (kPfWaves / heads_per_wg);
+  const int64_t cap = static_cast<int64_t>((prefill_workspace_bytes(a.num_seqs, a.total_q, a.group) -
+                                             static_cast<size_t>(kWsRecsInt) * 4) / (kRecInts * 4));
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a, sc.rows_per_wg,
+                     static_cast<int32_t>(cap), sc.ws);
+  // two persistent workgroups per CU (more could not be resident)
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t max_items = cap * a.num_kv_heads * sc.head_groups;
+  const int64_t grid = std::min<int64_t>(2 * static_cast<int64_t>(cus), max_items);
+  if (grid <= 0) return hipGetLastError();
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL(varlen_prefill_kernel<128>, grid, dim3(kPfThreads), 0, stream, a,
-                       heads_per_wg, head_groups, rows_per_wg, q_tiles);
+    hipLaunchKernelGGL(varlen_prefill_kernel<128>, dim3(static_cast<uint32_t>(grid)), dim3(kPfThreads), 0,
+                       stream, a, sc);
   } else {
-    hipLaunchKernelGGL(varlen_prefill_kernel<64>, grid, dim3(kPfThreads), 0, stream, a,
-                       heads_per_wg, head_groups, rows_per_wg, q_tiles);
+    hipLaunchKernelGGL(varlen_prefill_kernel<64>, dim3(static_cast<uint32_t>(grid)), dim3(kPfThreads), 0,
+                       stream, a, sc);
   }
   return hipGetLastError();
 }

@@ -92,10 +92,12 @@ def test_decode_plan(lib):
     assert pkv.decode_split_tokens(4, 8, 2, 64, 700) == 256
 
 
-def _prefill(lib, ns=2, tq=10, mq=5, mk=5, hq=4, hkv=2, d=64, bs=16, mb=1, causal=1, out=16):
+def _prefill(lib, ns=2, tq=10, mq=5, mk=5, hq=4, hkv=2, d=64, bs=16, mb=1, causal=1, out=16,
+             ws=16, ws_bytes=1 << 20):
     p = ctypes.c_void_p(16)
     return lib.pkv_varlen_prefill_attention(ctypes.c_void_p(out), p, p, p, p, p, p, ns, tq, mq, mk,
-                                            hq, hkv, d, bs, mb, 0.125, causal, None)
+                                            hq, hkv, d, bs, mb, 0.125, causal, ctypes.c_void_p(ws),
+                                            ws_bytes, None)
 
 
 def test_prefill_argument_checks(lib):
@@ -106,6 +108,20 @@ def test_prefill_argument_checks(lib):
     assert _prefill(lib, out=0) == binding.PKV_ERR_INVALID_ARG
     assert _prefill(lib, ns=0) == binding.PKV_OK
     assert _prefill(lib, tq=0) == binding.PKV_OK
+    assert _prefill(lib, ws=0) == binding.PKV_ERR_INVALID_ARG           # no workspace
+    assert _prefill(lib, ws_bytes=64) == binding.PKV_ERR_INVALID_ARG    # too small
+    assert _prefill(lib, ws=24) == binding.PKV_ERR_INVALID_ARG          # misaligned
+
+
+def test_prefill_workspace_size():
+    # counters + pair count (1088 bytes), then 64 bytes per (sequence, q tile) pair; at GQA
+    # ratio 4 a workgroup covers 32 query rows, at ratio 2 64, without GQA 128
+    assert pkv.prefill_workspace_bytes(0, 0, 32, 8) == 0
+    assert pkv.prefill_workspace_bytes(64, 35931, 32, 8) == 1088 + 64 * ((35931 + 31) // 32 + 64)
+    assert pkv.prefill_workspace_bytes(3, 300, 8, 4) == 1088 + 64 * ((300 + 63) // 64 + 3)
+    assert pkv.prefill_workspace_bytes(3, 300, 8, 8) == 1088 + 64 * ((300 + 127) // 128 + 3)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.prefill_workspace_bytes(1, 10, 6, 4)
 
 
 def test_binding_rejects_host_tensors(lib):
