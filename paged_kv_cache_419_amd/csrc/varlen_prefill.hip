@@ -169,7 +169,7 @@ template <int D>
 struct WaveState {
   u32x4 qb[PrefillShape<D>::KS];      // B operand Q^T per k-step
   f32x16 o[PrefillShape<D>::DC];      // O^T accumulators
-  f32x16 lsum;                        // row sums of the bf16 weights (every element of a lane's column alike)
+  float lsum;                         // this lane's share of its row's weight sum (the other half: lane ^ 32)
   float m;                            // running reference max (log2 domain) of this lane's row
 };
 
@@ -200,12 +200,18 @@ __device__ __forceinline__ void sched_reads_ahead() {
 // Weights exp2(s c - m) of one 64-key tile, rounded to bf16 and packed in
 // the B-operand order of the PV product: 16-key block u = 2 kb + hb, k-slots
 // 0..3 are keys 16u + 4h + i, k-slots 4..7 are keys 16u + 8 + 4h + i.
-__device__ __forceinline__ void tile_weights(const f32x16 (&s)[kPfKB], u32x4 (&pb)[kPfU], float m, float c) {
+// Returns the sum of this lane's 32 weights (fp32, before rounding).
+__device__ __forceinline__ float tile_weights(const f32x16 (&s)[kPfKB], u32x4 (&pb)[kPfU], float m, float c) {
+  float sum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < kPfKB; ++kb) {
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = fast_exp2(__builtin_fmaf(s[kb][v], c, -m));
+    float part[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[j] = (p[4 * j] + p[4 * j + 1]) + (p[4 * j + 2] + p[4 * j + 3]);
+    sum += (part[0] + part[1]) + (part[2] + part[3]);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int j = 2 * hb;
@@ -214,6 +220,7 @@ __device__ __forceinline__ void tile_weights(const f32x16 (&s)[kPfKB], u32x4 (&p
                               pack_bf16x2(p[4 * j + 6], p[4 * j + 7])};
     }
   }
+  return sum;
 }
 
 // True when some packed bf16 weight is >= 2^kRescaleSlack (or inf / NaN):
@@ -289,7 +296,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
     w.m = mx * (c * sgn);
   }
   u32x4 pb[kPfU];
-  tile_weights(s, pb, w.m, c);
+  float tsum = tile_weights(s, pb, w.m, c);
   if (__ballot(weights_overflow(pb)) != 0) {
     float mx = s[0][0] * sgn;
 #pragma unroll
@@ -303,12 +310,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
 #pragma unroll
     for (int cb = 0; cb < S::DC; ++cb) w.o[cb] *= alpha;
     w.m = m_new;
-    tile_weights(s, pb, w.m, c);
+    tsum = tile_weights(s, pb, w.m, c);
   }
-  // row sums on the matrix cores: (all-ones)^T P^T
-  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-#pragma unroll
-  for (int u = 0; u < kPfU; ++u) w.lsum = mfma32x32x16(ones, pb[u], w.lsum);
+  w.lsum += tsum;
 #pragma unroll
   for (int u = 0; u < kPfU; ++u) {
 #pragma unroll
@@ -318,7 +322,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
       w.o[cb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[u], w.o[cb]);
     }
   }
-  sched_reads_ahead<kPfU * S::DC + kPfU, 2 * kPfU * S::DC, 8>();
+  sched_reads_ahead<kPfU * S::DC, 2 * kPfU * S::DC, 8>();
 }
 
 // Start of tile step t: wait for this wave's loads of tile t (younger tiles
@@ -648,7 +652,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
 #pragma unroll
     for (int cb = 0; cb < S::DC; ++cb) w.o[cb] = f32x16{};
     w.m = -INFINITY;
-    w.lsum = f32x16{};
+    w.lsum = 0.f;
 
     // Start of ring step T (tile t of this item): wait for this wave's loads
     // of the tile (at an item's first tile, the previous item's output stores,
@@ -713,7 +717,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
     // of this head, so the padding rows' stores are dropped by the hardware
     // (the count of store instructions stays kStores, whatever the rows).
     {
-      const float lt = w.lsum[0];  // the sum over all keys of this lane's row
+      const float lt = w.lsum + __shfl_xor(w.lsum, 32);  // the sum over all keys of this lane's row
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const uint32_t hrow = static_cast<uint32_t>(a.num_q_heads) * D * 2;  // bytes per token row
       const char* ob = static_cast<const char*>(a.out) +
