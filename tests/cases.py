@@ -39,6 +39,24 @@ def small_workloads():
     cases["prefill_prefix_bs16"] = W.prefill([3, 20], prefix_len=32, num_q_heads=2,
                                              num_kv_heads=1, head_dim=64, block_size=16, seed=16,
                                              name="prefill_prefix_bs16")
+    # scales the pages never use (negative, zero), full (non-causal) attention, GQA ratios
+    # 1, 3 and 8, and enough query tiles that every prefill workgroup runs several items
+    cases["prefill_negscale_g4"] = W.prefill([20, 70, 1], num_q_heads=8, num_kv_heads=2,
+                                             head_dim=128, block_size=32, seed=17, scale=-0.3,
+                                             name="prefill_negscale_g4")
+    cases["prefill_scale0_mha"] = W.prefill([9, 150], num_q_heads=2, num_kv_heads=2,
+                                            head_dim=64, block_size=16, seed=18, scale=0.0,
+                                            name="prefill_scale0_mha")
+    cases["prefill_full_g3"] = W.prefill([12, 40, 0, 5], hist=[30, 0, 0, 9], num_q_heads=6,
+                                         num_kv_heads=2, head_dim=64, block_size=16, seed=19,
+                                         causal=False, name="prefill_full_g3")
+    lens = np.random.Generator(np.random.PCG64(20)).integers(1, 300, size=48, endpoint=True)
+    cases["prefill_g8_many"] = W.prefill(lens.tolist(), num_q_heads=16, num_kv_heads=2,
+                                         head_dim=64, block_size=64, seed=20,
+                                         name="prefill_g8_many")
+    cases["decode_negscale"] = W.decode([3, 40, 257], num_q_heads=8, num_kv_heads=4,
+                                        head_dim=128, block_size=16, seed=22, scale=-0.5,
+                                        name="decode_negscale")
     return cases
 
 

@@ -7,6 +7,7 @@ and checks that some pin catches each one.
 """
 from __future__ import annotations
 
+import dataclasses
 import json
 import math
 import os
@@ -209,6 +210,10 @@ def pin_torch_sdpa(name):
         causal = w.kind == "prefill" and w.causal
         if lk == 0 or lq == 0 or (causal and lq != lk):
             continue
+        if w.scale <= 0:
+            # torch's math path scales the masked (-inf) scores too, so a non-positive
+            # scale turns its mask into +inf / NaN; those cases have pins of their own
+            continue
         qd, kd, vd = (torch.from_numpy(_f64(x)).transpose(0, 1)[None] for x in w.dense(s))
         ref = torch.nn.functional.scaled_dot_product_attention(
             qd.contiguous(), kd.contiguous(), vd.contiguous(), is_causal=causal,
@@ -216,6 +221,43 @@ def pin_torch_sdpa(name):
         assert np.abs(ref - _rows_of(w, out, s)).max() < 1e-12
         checked += 1
     return checked
+
+
+def pin_scale_zero_mean(name):
+    """Scale 0: every visible key has the same score, so each row is the mean of
+    the V rows it sees (causal limit included)."""
+    w = cases.get(name)
+    assert w.scale == 0.0
+    out = cases.run_oracle(w, cases.inputs(name))
+    g = w.num_q_heads // w.num_kv_heads
+    for s in range(w.num_seqs):
+        lq, lk = int(w.lq[s]), int(w.lk[s])
+        if lq == 0:
+            continue
+        _, _, vd = w.dense(s)
+        v = _f64(vd)  # [Lk, Hkv, d]
+        rows = _rows_of(w, out, s)
+        for r in range(rows.shape[0]):
+            n = (lk - lq + r + 1) if (w.kind == "prefill" and w.causal) else lk
+            for h in range(w.num_q_heads):
+                ref = v[:n, h // g].mean(axis=0) if n > 0 else np.zeros(w.head_dim)
+                assert np.abs(rows[r, h] - ref).max() < 1e-12
+
+
+def pin_negative_scale(name):
+    """softmax(scale * q.k) with scale < 0 equals the attention of -q at -scale > 0
+    (exact in fp64: negating q and the scale changes no magnitude)."""
+    w = cases.get(name)
+    assert w.scale < 0
+    h = cases.inputs(name)
+    out = cases.run_oracle(w, h)
+    h2 = dict(h)
+    h2["q"] = h["q"] ^ np.uint16(0x8000)
+    out2 = cases.run_oracle(dataclasses.replace(w, scale=-w.scale), h2)
+    assert np.array_equal(out, out2)
+    # and it is not the attention at |scale| (the sign matters)
+    out3 = cases.run_oracle(dataclasses.replace(w, scale=-w.scale), h)
+    assert np.abs(out3 - out).max() > 1e-3
 
 
 def pin_closed_forms():
@@ -254,16 +296,17 @@ def pin_closed_forms():
 
 
 def pin_decode_is_last_prefill_row(name):
-    """Prefill row r equals a decode of that query over keys 0 .. off + r."""
+    """Prefill row r equals a decode of that query over keys 0 .. off + r (all Lk keys
+    without the causal limit)."""
     w = cases.get(name)
-    assert w.kind == "prefill" and w.causal
+    assert w.kind == "prefill"
     h = cases.inputs(name)
     out = cases.run_oracle(w, h)
     for s in range(w.num_seqs):
         lq, lk = int(w.lq[s]), int(w.lk[s])
         q0 = int(w.cu_seqlens_q[s])
         for r in sorted({0, lq // 2, lq - 1}) if lq else []:
-            ctx = np.array([lk - lq + r + 1], np.int32)
+            ctx = np.array([lk - lq + r + 1 if w.causal else lk], np.int32)
             dec = oracle.paged_decode(h["q"][q0 + r:q0 + r + 1], h["k_cache_stored"],
                                       h["v_cache_stored"], h["block_tables"][s:s + 1], ctx,
                                       w.block_size, w.scale)

@@ -65,6 +65,15 @@ def test_closed_forms():
     P.pin_closed_forms()
 
 
+def test_scale_zero_is_mean_of_visible_values():
+    P.pin_scale_zero_mean("prefill_scale0_mha")
+
+
+@pytest.mark.parametrize("name", ["prefill_negscale_g4", "decode_negscale"])
+def test_negative_scale(name):
+    P.pin_negative_scale(name)
+
+
 @pytest.mark.parametrize("name", PREFILL)
 def test_decode_is_last_prefill_row(name):
     P.pin_decode_is_last_prefill_row(name)
