@@ -342,6 +342,25 @@ def main():
     }
     if decode:
         rec["decode_tok_per_s"] = w.num_seqs / (ms_step * 1e-3)
+        if int(w.lq.min()) == 1 and w.pad_tokens == 0 and not args.copy_probe:
+            # the same step as one fused kernel (store the new tokens and attend)
+            def fused(c, out):
+                pkv.store_and_decode(out, c["q"], c["k_new"], c["v_new"], c["k_cache"], c["v_cache"],
+                                     c["slot_mapping"], c["block_tables"], c["context_lens"],
+                                     w.block_size, w.max_context_len, w.scale, split, workspace)
+            for i in range(args.warmup):
+                fused(copies[i % reps], outs[i % reps])
+            torch.cuda.synchronize()
+            f0 = torch.cuda.Event(enable_timing=True)
+            f1 = torch.cuda.Event(enable_timing=True)
+            f0.record(stream)
+            for i in range(args.steps):
+                fused(copies[i % reps], outs[i % reps])
+            f1.record(stream)
+            torch.cuda.synchronize()
+            H.check_against_oracle(w, outs[0], probe)
+            rec["fused_ms_per_step"] = f0.elapsed_time(f1) / args.steps
+            rec["fused_decode_tok_per_s"] = w.num_seqs / (rec["fused_ms_per_step"] * 1e-3)
         if args.graph:
             # the same step (store + decode) captured once per input copy and replayed
             graphs = []

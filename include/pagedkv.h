@@ -7,6 +7,8 @@
  *                                 block-paged cache at its slot-mapping entry
  *   pkv_paged_decode_attention    one query token per sequence attending to its
  *                                 whole cached history through its block table
+ *   pkv_store_and_decode          both of the above for one decode step, in one
+ *                                 kernel
  *   pkv_varlen_prefill_attention  causal attention over packed variable-length
  *                                 prompts (cu_seqlens), keys read through block
  *                                 tables, so blocks shared by prefix caching are
@@ -133,6 +135,39 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
                                       float scale, int32_t split_tokens, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * Fused decode step: for each sequence b, store its new token (row b of k_new
+ * / v_new) into cache slot slot_mapping[b] and attend q[b] over positions
+ * 0 .. context_lens[b]-1, the last of which is that new token -- the result
+ * of pkv_store_kvcache followed by pkv_paged_decode_attention, in one launch
+ * (the cache image is the same bit for bit; the output differs at most in
+ * fp32 rounding order, as the new token is folded into the softmax state
+ * last) ("Nano-vLLM
+ * part 1", section 5.2: a decode step hands the slot mapping and the context
+ * lengths to the GPU; hotdry.top, PagedAttention section: the store kernel,
+ * and the low-level section: the KV-cache decode call).  The new token is
+ * attended from k_new / v_new, not re-read from the cache, so
+ * slot_mapping[b] is expected to be the slot of position context_lens[b]-1 in
+ * block_tables[b] (the attention result does not depend on it).
+ *
+ *   k_new, v_new  device bf16 [batch, num_kv_heads, head_dim]
+ *   slot_mapping  device int32 [batch]; negative entries (padding) and
+ *                 entries >= num_slots store nothing
+ *   num_slots     rows of each cache (num_blocks * block_size)
+ *   other arguments as for pkv_paged_decode_attention (workspace sized by
+ *   pkv_decode_workspace_bytes); k_cache / v_cache are written.
+ * A row with context_lens[b] == 0 still stores its token and gets a zero
+ * output row.
+ */
+pkv_status pkv_store_and_decode(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, int64_t num_slots, float scale,
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /*
  * Bytes of device workspace pkv_varlen_prefill_attention needs for these

@@ -24,6 +24,7 @@ EXPORTS = (
     "pkv_decode_workspace_bytes",
     "pkv_decode_split_tokens",
     "pkv_paged_decode_attention",
+    "pkv_store_and_decode",
     "pkv_prefill_workspace_bytes",
     "pkv_varlen_prefill_attention",
     "pkv_last_error",
@@ -59,6 +60,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pkv_paged_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                i32, i32, f32, i32, vp, sz, vp]
     lib.pkv_paged_decode_attention.restype = ctypes.c_int
+    lib.pkv_store_and_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                         i32, i32, i32, i64, f32, i32, vp, sz, vp]
+    lib.pkv_store_and_decode.restype = ctypes.c_int
     lib.pkv_prefill_workspace_bytes.argtypes = [i32, i64, i32, i32]
     lib.pkv_prefill_workspace_bytes.restype = sz
     lib.pkv_varlen_prefill_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
@@ -155,6 +159,35 @@ def paged_decode_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Te
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), b, hq, hkv, d, block_size, block_tables.shape[1], max_context_len,
         float(scale), split_tokens, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def store_and_decode(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                     k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                     block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,
+                     max_context_len: int, scale: float, split_tokens: int = 0,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One decode step in one kernel: store each sequence's new K/V row, then attend."""
+    for name, t in (("out", out), ("q", q), ("k_new", k_new), ("v_new", v_new),
+                    ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, torch.bfloat16, name, 3)
+    for name, t in (("slot_mapping", slot_mapping), ("context_lens", context_lens)):
+        _need(t, torch.int32, name, 1)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    b, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    if out.shape != q.shape or k_new.shape != (b, hkv, d) or v_new.shape != k_new.shape \
+            or k_cache.shape[2] != d or v_cache.shape != k_cache.shape \
+            or slot_mapping.shape[0] != b or block_tables.shape[0] != b or context_lens.shape[0] != b:
+        raise ValueError("store_and_decode: inconsistent shapes")
+    need = decode_workspace_bytes(b, hq, hkv, d, max_context_len, split_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pkv_store_and_decode(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), b, hq, hkv, d, block_size,
+        block_tables.shape[1], max_context_len, k_cache.shape[0], float(scale), split_tokens,
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def prefill_workspace_bytes(num_seqs: int, total_q: int, num_q_heads: int,

@@ -126,14 +126,19 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
   return static_cast<size_t>(batch) * num_q_heads * n * (head_dim + 2) * sizeof(float);
 }
 
-pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_cache,
-                                      const void* v_cache, const int32_t* block_tables,
-                                      const int32_t* context_lens, int32_t batch,
-                                      int32_t num_q_heads, int32_t num_kv_heads,
-                                      int32_t head_dim, int32_t block_size,
-                                      int32_t max_blocks_per_seq, int32_t max_context_len,
-                                      float scale, int32_t split_tokens, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by the decode call and the fused store + decode
+// call (k_new / v_new / slot_mapping are null for the former).
+pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t batch,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       float scale, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                       const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                       int64_t num_slots, bool fused, void* stream, const char* what) {
   if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch %d < 0", batch);
   pkv_status st = check_heads(num_q_heads, num_kv_heads, head_dim);
   if (st != PKV_OK) return st;
@@ -146,10 +151,14 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
   if (split_tokens < 0 || split_tokens % 32)
     return fail(PKV_ERR_INVALID_ARG, "split_tokens %d: 0 or a positive multiple of 32", split_tokens);
+  if (fused && num_slots <= 0) return fail(PKV_ERR_INVALID_ARG, "num_slots must be positive");
   if (batch == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+  if (fused && (!k_new || !v_new || !slot_mapping))
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (fused && (!aligned16(k_new) || !aligned16(v_new))))
     return fail(PKV_ERR_INVALID_ARG, "bf16 buffers must be 16-byte aligned");
   if (static_cast<int64_t>(num_kv_heads) * head_dim * 2 * 16 >= (int64_t{1} << 31))
     return fail(PKV_ERR_UNSUPPORTED, "num_kv_heads %d too large for 32-bit in-block offsets",
@@ -192,8 +201,44 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
   a.split_tokens = split;
   a.n_split = n;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(pkv::launch_paged_decode(a, static_cast<hipStream_t>(stream)),
-                    "paged_decode_attention launch");
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.num_slots = num_slots;
+  a.fused = fused ? 1 : 0;
+  return hip_status(pkv::launch_paged_decode(a, static_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t batch,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, int32_t split_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, batch, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
+                     scale, split_tokens, workspace, workspace_bytes, nullptr, nullptr, nullptr, 0,
+                     false, stream, "paged_decode_attention launch");
+}
+
+pkv_status pkv_store_and_decode(void* out, const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, int64_t num_slots, float scale,
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, batch, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
+                     scale, split_tokens, workspace, workspace_bytes, k_new, v_new, slot_mapping,
+                     num_slots, true, stream, "store_and_decode launch");
 }
 
 size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int64_t total_q, int32_t num_q_heads,

@@ -28,6 +28,14 @@ struct DecodeArgs {
   int32_t split_tokens;
   int32_t n_split;
   float scale_log2;     // scale * log2(e)
+  // Fused store (all null / 0 otherwise): the new token of sequence b is row b
+  // of k_new / v_new; it is attended from there and written to cache slot
+  // slot_mapping[b] (skipped when outside [0, num_slots)).
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
+  int64_t num_slots;
+  int32_t fused;
 };
 
 // Decode plan shared by the workspace query and the launch.

@@ -114,6 +114,29 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* kc, co
   }
 }
 
+// The fused call's new token as a tile of its own: row 0 of the tile is this
+// kv head's row of k_new / v_new (whose rows have the cache's row stride, so
+// the per-lane offsets are the same); the other rows fall outside the
+// descriptors and read as zeros.
+template <int D>
+__device__ __forceinline__ void load_new_token(TileRegs<D>& r, const uint16_t* kn, const uint16_t* vn,
+                                               uint32_t koff, const uint32_t (&voff)[DecodeShape<D>::VLOADS]) {
+  using S = DecodeShape<D>;
+  const buffer_rsrc k0 = make_rsrc(kn, D * 2);
+  const buffer_rsrc v0 = make_rsrc(vn, D * 2);
+  const buffer_rsrc none = make_rsrc(kn, 0);
+#pragma unroll
+  for (int kk = 0; kk < S::KK; ++kk) {
+    r.k[0][kk] = buffer_load16(k0, koff + 64 * kk);
+    r.k[1][kk] = buffer_load16(none, koff + 64 * kk);
+  }
+#pragma unroll
+  for (int e = 0; e < S::VLOADS; ++e) {
+    const bool second = e * S::ROWS_PER_LOAD >= 16;
+    r.v[e] = buffer_load16(second ? none : v0, voff[e]);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void compute_tile(const TileRegs<D>& r, const u32x4 (&qb)[DecodeShape<D>::KK],
                                              f32x4 (&o)[DecodeShape<D>::DB], float& m, float& lsum,
@@ -217,13 +240,33 @@ __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs
   const int h0 = g * a.group + hg * 16;
   uint16_t* out = static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(b) * a.num_q_heads + h0) * D;
 
+  // Fused call: the last position (the new token) is attended from k_new /
+  // v_new, and the workgroup of head group 0 whose split holds it stores this
+  // kv head's new K and V rows into cache slot slot_mapping[b].  No workgroup
+  // of the call reads that slot.
+  const bool last_split = split == max(0, ctx - 1) / a.split_tokens;
+  const int64_t nrow = (static_cast<int64_t>(b) * a.num_kv_heads + g) * D;
+  const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + nrow;
+  const uint16_t* vn = static_cast<const uint16_t*>(a.v_new) + nrow;
+  if (a.fused && last_split && hg == 0 && threadIdx.x < 2 * (D / 8)) {
+    const int64_t slot = a.slot_mapping[b];
+    if (slot >= 0 && slot < a.num_slots) {
+      const int piece = threadIdx.x % (D / 8);
+      const bool is_v = threadIdx.x >= D / 8;
+      uint16_t* dst = static_cast<uint16_t*>(const_cast<void*>(is_v ? a.v_cache : a.k_cache)) +
+                      (slot * a.num_kv_heads + g) * D + 8 * piece;
+      *reinterpret_cast<u32x4*>(dst) = ldg16((is_v ? vn : kn) + 8 * piece);
+    }
+  }
+
   if (t0 >= ctx) {
     if (a.n_split == 1) {  // empty context: a zero row
       for (int i = threadIdx.x; i < heads_here * D; i += kDecThreads) out[i] = 0;
     }
     return;
   }
-  const int t1 = min(ctx, t0 + a.split_tokens);
+  // end of the positions read from the cache (the fused call's new token is not)
+  const int t1 = a.fused ? min(ctx - 1, t0 + a.split_tokens) : min(ctx, t0 + a.split_tokens);
 
   // B operand of S^T = K Q^T: lane holds 8 values of query head n16.
   u32x4 qb[S::KK];
@@ -277,6 +320,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs
       __builtin_amdgcn_sched_barrier(0);
       compute_tile<D>(rb, qb, o, m, lsum, vst, j + kStride, t1, lane, a.scale_log2);
     }
+  }
+
+  if (a.fused && last_split && wave == kDecWaves - 1) {  // the new token, by one wave
+    TileRegs<D> rn;
+    load_new_token<D>(rn, kn, vn, koff, voff);
+    compute_tile<D>(rn, qb, o, m, lsum, vst, ctx - 1, ctx, lane, a.scale_log2);
   }
 
   // Merge the four waves' states.

@@ -9,8 +9,10 @@ captured as it is.  A batch of B sequences runs in the smallest bucket >= B;
 the padding rows carry slot -1 (the store skips them) and context length 0
 (decode writes zeros), so they touch no cache slot.
 
-This module only arranges static buffers and graph capture with torch; every
-step still runs in the HIP kernels of libpagedkv.so.
+With ``fused=True`` a step is the single store_and_decode kernel instead of
+the store and decode kernels.  This module only arranges static buffers and
+graph capture with torch; every step still runs in the HIP kernels of
+libpagedkv.so.
 """
 from __future__ import annotations
 
@@ -49,7 +51,8 @@ class DecodeGraphs:
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, num_q_heads: int,
                  block_size: int, max_blocks_per_seq: int, max_context_len: int, scale: float,
-                 buckets: Sequence[int] = DEFAULT_BUCKETS, split_tokens: int = 0):
+                 buckets: Sequence[int] = DEFAULT_BUCKETS, split_tokens: int = 0,
+                 fused: bool = False):
         if k_cache.shape != v_cache.shape or k_cache.dim() != 3:
             raise ValueError("k_cache and v_cache must both be [num_slots, num_kv_heads, head_dim]")
         self.k_cache, self.v_cache = k_cache, v_cache
@@ -60,6 +63,7 @@ class DecodeGraphs:
         self.max_context_len = max_context_len
         self.scale = scale
         self.split_tokens = split_tokens
+        self.fused = fused  # one kernel per step (store_and_decode) instead of two
         self.buckets = tuple(sorted(set(int(b) for b in buckets)))
         self._b: Dict[int, _Bucket] = {}
         dev = k_cache.device
@@ -72,6 +76,12 @@ class DecodeGraphs:
         self._capture_all()
 
     def _step(self, bk: _Bucket) -> None:
+        if self.fused:
+            binding.store_and_decode(bk.out, bk.q, bk.k, bk.v, self.k_cache, self.v_cache,
+                                     bk.slot_mapping, bk.block_tables, bk.context_lens,
+                                     self.block_size, self.max_context_len, self.scale,
+                                     self.split_tokens, bk.workspace)
+            return
         binding.store_kvcache(bk.k, bk.v, self.k_cache, self.v_cache, bk.slot_mapping)
         binding.paged_decode_attention(bk.out, bk.q, self.k_cache, self.v_cache, bk.block_tables,
                                        bk.context_lens, self.block_size, self.max_context_len,

@@ -88,3 +88,34 @@ def test_graph_bucket_choice_and_padding():
     slots = np.sort(w.slot_mapping[w.slot_mapping >= 0])
     assert np.array_equal(np.nonzero(changed.cpu().numpy())[0], slots)
     H.check_against_oracle(w, out, list(range(w.num_seqs)))
+
+
+def test_fused_graph_replays_match_eager_fused_call():
+    _note("fused graph replays")
+    w = W.decode([1, 17, 33, 64, 5, 90, 16], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                 block_size=16, seed=23, name="graph_fused_b7")
+    max_ctx = 96
+    tg = w.materialize("cuda")
+    graphs = DecodeGraphs(tg["k_cache"], tg["v_cache"], w.num_q_heads, w.block_size,
+                          w.max_blocks_per_seq, max_ctx, w.scale, buckets=(4, 8), fused=True)
+    for i, seqs in enumerate([list(range(7)), [0, 2, 4], list(range(7))]):
+        te = w.materialize("cuda")
+        idx = torch.tensor(seqs, device="cuda")
+        tin = {k: (te[k][idx] if k in ("q", "k_new", "v_new", "slot_mapping", "block_tables",
+                                        "context_lens") else te[k]) for k in te}
+        ref = torch.empty_like(tin["q"])
+        pkv.store_and_decode(ref, tin["q"], tin["k_new"], tin["v_new"], te["k_cache"], te["v_cache"],
+                             tin["slot_mapping"], tin["block_tables"], tin["context_lens"],
+                             w.block_size, max_ctx, w.scale)
+        got = graphs.run(tin["q"], tin["k_new"], tin["v_new"], tin["slot_mapping"],
+                         tin["block_tables"], tin["context_lens"]).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"step {i}"
+        assert torch.equal(tg["k_cache"].view(torch.int16)[tin["slot_mapping"].long()],
+                           tin["k_new"].view(torch.int16))
+        _ = (tin["q"].float() * 2).sum().item()
+        torch.cuda.synchronize()
+    got = graphs.run(tg["q"], tg["k_new"], tg["v_new"], tg["slot_mapping"], tg["block_tables"],
+                     tg["context_lens"]).clone()
+    torch.cuda.synchronize()
+    H.check_against_oracle(w, got, list(range(w.num_seqs)))

@@ -124,6 +124,25 @@ def test_prefill_workspace_size():
         pkv.prefill_workspace_bytes(1, 10, 6, 4)
 
 
+def _fused(lib, b=2, hq=4, hkv=2, d=64, bs=16, mb=2, ctx=20, slots=64, kn=16, sm=16, split=0):
+    p = ctypes.c_void_p(16)
+    return lib.pkv_store_and_decode(p, p, ctypes.c_void_p(kn), p, p, p, ctypes.c_void_p(sm), p, p,
+                                    b, hq, hkv, d, bs, mb, ctx, slots, 0.125, split, None, 0, None)
+
+
+def test_store_and_decode_argument_checks(lib):
+    assert _fused(lib, kn=0) == binding.PKV_ERR_INVALID_ARG             # no k_new
+    assert _fused(lib, sm=0) == binding.PKV_ERR_INVALID_ARG             # no slot_mapping
+    assert _fused(lib, kn=24) == binding.PKV_ERR_INVALID_ARG            # misaligned k_new
+    assert _fused(lib, slots=0) == binding.PKV_ERR_INVALID_ARG          # empty cache
+    assert _fused(lib, ctx=33) == binding.PKV_ERR_INVALID_ARG           # beyond the table
+    assert _fused(lib, split=48) == binding.PKV_ERR_INVALID_ARG         # not a multiple of 32
+    assert _fused(lib, d=96) == binding.PKV_ERR_UNSUPPORTED
+    assert _fused(lib, b=0) == binding.PKV_OK
+    # a split workspace is required once the context spans several splits
+    assert _fused(lib, ctx=64, split=32, mb=4) == binding.PKV_ERR_INVALID_ARG
+
+
 def test_binding_rejects_host_tensors(lib):
     import torch
     x = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
