@@ -217,6 +217,65 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
                                         float scale, int32_t causal, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Control plane: the block manager (host memory only, no GPU call).
+ *
+ * It decides which cache blocks each sequence uses and hands the data plane
+ * its block tables and slot mappings ("Nano-vLLM part 1", section 4: fixed-size
+ * blocks (4.1), prefix caching through a hash -> block id map with reference
+ * counts (4.2), CPU-side metadata, freed blocks not cleared (4.3); section 3.2:
+ * preemption when no block is left).  A full block's hash covers its tokens
+ * and the hash of the block before it; a new sequence reuses the cached blocks
+ * of its longest cached block-aligned prefix (always leaving at least one
+ * block to compute); free blocks are handed out oldest-freed first, and a
+ * freed block keeps its cached content until it is handed out again.  Not
+ * thread-safe: one caller at a time per manager.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+#define PKV_BM_NO_SPACE (-1) /* not enough free blocks; nothing was changed */
+#define PKV_BM_ERR_ARG (-2)  /* invalid argument or unknown / duplicate sequence id */
+
+/* A manager of num_blocks blocks of block_size tokens (NULL on bad sizes). */
+pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size);
+void pkv_bm_destroy(pkv_block_manager* m);
+
+/* Blocks that are free (cached content or not). */
+int32_t pkv_bm_num_free(const pkv_block_manager* m);
+
+/* Admit sequence seq_id with its n prompt tokens (host int32 ids): reuse the
+ * cached blocks of its prefix, take free blocks for the rest.  Returns the
+ * number of leading tokens whose K/V are already cached (a multiple of
+ * block_size; the prefill computes and stores tokens from there on), or
+ * PKV_BM_NO_SPACE / PKV_BM_ERR_ARG. */
+int32_t pkv_bm_allocate(pkv_block_manager* m, int64_t seq_id, const int32_t* tokens, int32_t n);
+
+/* Append one generated token to seq_id (a new block when the last one is
+ * full).  0, or PKV_BM_NO_SPACE (the caller preempts a sequence and retries)
+ * or PKV_BM_ERR_ARG. */
+int32_t pkv_bm_append(pkv_block_manager* m, int64_t seq_id, int32_t token);
+
+/* Release seq_id's blocks (finished or preempted).  0 or PKV_BM_ERR_ARG. */
+int32_t pkv_bm_free(pkv_block_manager* m, int64_t seq_id);
+
+/* Tokens of seq_id, or PKV_BM_ERR_ARG. */
+int32_t pkv_bm_seq_len(const pkv_block_manager* m, int64_t seq_id);
+
+/* Writes seq_id's block table into out[0 .. max_blocks-1] (-1 past its last
+ * block; out may be NULL) and returns its number of blocks, or
+ * PKV_BM_ERR_ARG. */
+int32_t pkv_bm_block_table(const pkv_block_manager* m, int64_t seq_id, int32_t* out,
+                           int32_t max_blocks);
+
+/* Slots of positions from .. to-1 of seq_id
+ * (block_table[p / block_size] * block_size + p % block_size) into out;
+ * returns to - from, or PKV_BM_ERR_ARG. */
+int32_t pkv_bm_slots(const pkv_block_manager* m, int64_t seq_id, int32_t from, int32_t to,
+                     int32_t* out);
+
+/* Reference count of a block (sequences using it), or PKV_BM_ERR_ARG. */
+int32_t pkv_bm_ref_count(const pkv_block_manager* m, int32_t block_id);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* pkv_last_error(void);
 

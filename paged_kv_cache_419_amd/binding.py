@@ -29,6 +29,16 @@ EXPORTS = (
     "pkv_varlen_prefill_attention",
     "pkv_last_error",
     "pkv_version",
+    "pkv_bm_create",
+    "pkv_bm_destroy",
+    "pkv_bm_num_free",
+    "pkv_bm_allocate",
+    "pkv_bm_append",
+    "pkv_bm_free",
+    "pkv_bm_seq_len",
+    "pkv_bm_block_table",
+    "pkv_bm_slots",
+    "pkv_bm_ref_count",
 )
 
 
@@ -68,6 +78,27 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pkv_varlen_prefill_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                                  i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.pkv_varlen_prefill_attention.restype = ctypes.c_int
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.pkv_bm_create.argtypes = [i32, i32]
+    lib.pkv_bm_create.restype = vp
+    lib.pkv_bm_destroy.argtypes = [vp]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_num_free.argtypes = [vp]
+    lib.pkv_bm_num_free.restype = i32
+    lib.pkv_bm_allocate.argtypes = [vp, i64, i32p, i32]
+    lib.pkv_bm_allocate.restype = i32
+    lib.pkv_bm_append.argtypes = [vp, i64, i32]
+    lib.pkv_bm_append.restype = i32
+    lib.pkv_bm_free.argtypes = [vp, i64]
+    lib.pkv_bm_free.restype = i32
+    lib.pkv_bm_seq_len.argtypes = [vp, i64]
+    lib.pkv_bm_seq_len.restype = i32
+    lib.pkv_bm_block_table.argtypes = [vp, i64, i32p, i32]
+    lib.pkv_bm_block_table.restype = i32
+    lib.pkv_bm_slots.argtypes = [vp, i64, i32, i32, i32p]
+    lib.pkv_bm_slots.restype = i32
+    lib.pkv_bm_ref_count.argtypes = [vp, i32]
+    lib.pkv_bm_ref_count.restype = i32
     lib.pkv_last_error.argtypes = []
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.argtypes = []

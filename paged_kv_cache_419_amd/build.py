@@ -21,6 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
 SOURCES = ["api.hip", "store_kvcache.hip", "paged_decode.hip", "varlen_prefill.hip"]
+HOST_SOURCES = ["block_manager.cpp"]  # host-only code, built with the host compiler
 ARCH = "gfx950"
 
 
@@ -53,10 +54,23 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _compile_host(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cxx = shutil.which("g++") or "c++"
+    cmd = [cxx, "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", "-c",
+           os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n" + res.stdout + res.stderr)
+    if res.stdout or res.stderr:
+        print(res.stdout + res.stderr, file=sys.stderr)
+    return obj
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + len(HOST_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES)) + list(ex.map(_compile_host, HOST_SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

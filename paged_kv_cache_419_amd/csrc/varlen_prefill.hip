@@ -48,6 +48,7 @@ constexpr int kPfU = kPfKeys / 16;   // 16-key k-blocks of the PV product per ti
 constexpr int kPfRows = 32;  // query rows per wave (the N side of a 32x32 MFMA)
 constexpr float kRescaleSlack = 8.f;  // log2 headroom of the lazy softmax rescale
 constexpr unsigned short kSlackBf16Bits = 0x4380;  // bf16 bit pattern of 2^kRescaleSlack
+static_assert(kSlackBf16Bits == (127 + static_cast<int>(kRescaleSlack)) << 7, "bf16 of 2^slack");
 
 template <int D>
 struct PrefillShape {
