@@ -214,6 +214,66 @@ def cpu_baseline(w, budget_s: float):
                       f"one thread), {t_work:.1f} s of oracle time; input generation untimed"}
 
 
+# ---- sampling (the adjacent next-token step) ----------------------------------------------
+SAMPLE_WORKLOAD = "sample_b256"
+
+
+def sample_bytes(logits: np.ndarray, top_k: int) -> int:
+    """Every logit read once, the noise of the candidates, one token id written per row."""
+    rows, vocab = logits.shape
+    return rows * (vocab * 4 + top_k * 4 + 4)
+
+
+def run_sampling(args, torch, pkv, dev):
+    from workload.sample import SAMPLE_ROWS, SAMPLE_TEMPERATURE, SAMPLE_TOP_K, SAMPLE_VOCAB, sample_inputs
+    logits, gumbel = sample_inputs(SAMPLE_ROWS, SAMPLE_VOCAB, seed=4196)
+    reps = args.replicas or 2  # 2 x 311 MB: no step finds its rows in the Infinity Cache
+    lg = [torch.from_numpy(logits).to(dev) for _ in range(reps)]
+    gg = [torch.from_numpy(gumbel).to(dev) for _ in range(reps)]
+    tok = [torch.empty(SAMPLE_ROWS, dtype=torch.int32, device=dev) for _ in range(reps)]
+    for i in range(args.warmup):
+        pkv.topk_sample(tok[i % reps], lg[i % reps], gg[i % reps], SAMPLE_TOP_K, SAMPLE_TEMPERATURE)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        pkv.topk_sample(tok[i % reps], lg[i % reps], gg[i % reps], SAMPLE_TOP_K, SAMPLE_TEMPERATURE)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+    call_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    import oracle.sampling as OS
+    want = OS.topk_sample(logits, gumbel, SAMPLE_TOP_K, SAMPLE_TEMPERATURE)
+    assert np.array_equal(tok[0].cpu().numpy(), want), "sampled tokens differ from the oracle"
+    nbytes = sample_bytes(logits, SAMPLE_TOP_K)
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "next-token sampling HBM GB/s (% peak)", "value": nbytes / (ms * 1e-3) / 1e9,
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": SAMPLE_WORKLOAD, "rows": SAMPLE_ROWS, "vocab": SAMPLE_VOCAB,
+                   "top_k": SAMPLE_TOP_K, "temperature": SAMPLE_TEMPERATURE,
+                   "input_copies_rotated": reps, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "topk_sample",
+                     "kernel_ms": call_ms},
+        "rows_per_s": SAMPLE_ROWS / (ms * 1e-3),
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        n = 0
+        while n < SAMPLE_ROWS and time.perf_counter() - t0 < args.cpu_budget:
+            OS.topk_sample(logits[n:n + 1], gumbel[n:n + 1], SAMPLE_TOP_K, SAMPLE_TEMPERATURE)
+            n += 1
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": n * (nbytes / SAMPLE_ROWS) / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} of {SAMPLE_ROWS} rows (NumPy, one thread), {dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 # ---- GPU run ----------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -252,6 +312,9 @@ def main():
     pkv.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == SAMPLE_WORKLOAD:
+        run_sampling(args, torch, pkv, dev)
+        return
     w = W.make(args.workload)
     decode = w.kind == "decode"
     work_set = (decode_bytes(w) if decode else prefill_bytes(w)) + store_bytes(w)

@@ -9,6 +9,7 @@
  *                                 whole cached history through its block table
  *   pkv_store_and_decode          both of the above for one decode step, in one
  *                                 kernel
+ *   pkv_topk_sample               temperature / top-k sampling of the next token
  *   pkv_varlen_prefill_attention  causal attention over packed variable-length
  *                                 prompts (cu_seqlens), keys read through block
  *                                 tables, so blocks shared by prefix caching are
@@ -216,6 +217,30 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
                                         int32_t block_size, int32_t max_blocks_per_seq,
                                         float scale, int32_t causal, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/*
+ * Next-token sampling with temperature and top-k ("Nano-vLLM part 1",
+ * section 5.4: the logits over the vocabulary become one token by sampling,
+ * the temperature reshaping softmax(logits / T); hotdry.top, configuration
+ * section: top_k bounds the candidates per step).  For each row r:
+ *   candidates: entries whose logit is >= the top_k-th largest logit of the
+ *     row (ties at that value all kept; every entry when top_k <= 0 or
+ *     top_k >= vocab), the order being that of the fp32 values with
+ *     -0 below +0;
+ *   tokens[r] = the candidate i maximising fl(fl(logits[r][i] * fl(1/T)) +
+ *     gumbel[r][i]) (each operation rounded in fp32, ties to the smallest i),
+ *     which draws from softmax(logits / T) restricted to the candidates when
+ *     gumbel holds independent standard Gumbel noise (the Gumbel-max identity);
+ *   temperature <= 0: tokens[r] = the first index of the row's maximum logit.
+ *
+ *   tokens   device int32 [rows]
+ *   logits   device fp32 [rows, vocab], finite or -inf (no NaN)
+ *   gumbel   device fp32 [rows, vocab] (may be NULL when temperature <= 0);
+ *            only the candidates' entries are read
+ * rows == 0 is a no-op.  vocab and rows must be below 2^31.
+ */
+pkv_status pkv_topk_sample(int32_t* tokens, const float* logits, const float* gumbel, int64_t rows,
+                           int64_t vocab, int32_t top_k, float temperature, void* stream);
 
 /* ------------------------------------------------------------------------
  * Control plane: the block manager (host memory only, no GPU call).

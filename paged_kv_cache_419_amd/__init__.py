@@ -8,6 +8,5 @@ tensors into the C calls.
 from .binding import (  # noqa: F401
     EXPORTS, LIB_PATH, PagedKVError, decode_split_tokens, decode_workspace_bytes, load,
     paged_decode_attention, prefill_workspace_bytes, store_and_decode, store_kvcache,
-    varlen_prefill_attention,
-    version,
+    topk_sample, varlen_prefill_attention, version,
 )

@@ -25,6 +25,7 @@ EXPORTS = (
     "pkv_decode_split_tokens",
     "pkv_paged_decode_attention",
     "pkv_store_and_decode",
+    "pkv_topk_sample",
     "pkv_prefill_workspace_bytes",
     "pkv_varlen_prefill_attention",
     "pkv_last_error",
@@ -73,6 +74,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pkv_store_and_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                          i32, i32, i32, i64, f32, i32, vp, sz, vp]
     lib.pkv_store_and_decode.restype = ctypes.c_int
+    lib.pkv_topk_sample.argtypes = [vp, vp, vp, i64, i64, i32, f32, vp]
+    lib.pkv_topk_sample.restype = ctypes.c_int
     lib.pkv_prefill_workspace_bytes.argtypes = [i32, i64, i32, i32]
     lib.pkv_prefill_workspace_bytes.restype = sz
     lib.pkv_varlen_prefill_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
@@ -219,6 +222,22 @@ def store_and_decode(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_
         _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), b, hq, hkv, d, block_size,
         block_tables.shape[1], max_context_len, k_cache.shape[0], float(scale), split_tokens,
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def topk_sample(tokens: torch.Tensor, logits: torch.Tensor, gumbel: Optional[torch.Tensor],
+                top_k: int, temperature: float, stream=None) -> None:
+    """One token per row of ``logits`` (fp32 [rows, vocab]) into ``tokens`` (int32 [rows])."""
+    _need(logits, torch.float32, "logits", 2)
+    _need(tokens, torch.int32, "tokens", 1)
+    rows, vocab = logits.shape
+    if tokens.shape[0] != rows:
+        raise ValueError("topk_sample: tokens must have one entry per row")
+    if gumbel is not None:
+        _need(gumbel, torch.float32, "gumbel", 2)
+        if gumbel.shape != logits.shape:
+            raise ValueError("topk_sample: gumbel must have the shape of logits")
+    _check(load().pkv_topk_sample(_ptr(tokens), _ptr(logits), _ptr(gumbel), rows, vocab, int(top_k),
+                                  float(temperature), _stream(stream)))
 
 
 def prefill_workspace_bytes(num_seqs: int, total_q: int, num_q_heads: int,

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["api.hip", "store_kvcache.hip", "paged_decode.hip", "varlen_prefill.hip"]
+SOURCES = ["api.hip", "store_kvcache.hip", "paged_decode.hip", "varlen_prefill.hip", "sampling.hip"]
 HOST_SOURCES = ["block_manager.cpp"]  # host-only code, built with the host compiler
 ARCH = "gfx950"
 

@@ -227,6 +227,29 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
                      false, stream, "paged_decode_attention launch");
 }
 
+pkv_status pkv_topk_sample(int32_t* tokens, const float* logits, const float* gumbel, int64_t rows,
+                           int64_t vocab, int32_t top_k, float temperature, void* stream) {
+  if (rows < 0 || vocab <= 0) return fail(PKV_ERR_INVALID_ARG, "rows < 0 or vocab <= 0");
+  if (!std::isfinite(temperature)) return fail(PKV_ERR_INVALID_ARG, "temperature is not finite");
+  const bool greedy = temperature <= 0.f;
+  const float inv_t = greedy ? 0.f : 1.0f / temperature;
+  if (!std::isfinite(inv_t)) return fail(PKV_ERR_INVALID_ARG, "temperature too small: 1/T overflows");
+  if (vocab > (int64_t{1} << 31) - 1 || rows > (int64_t{1} << 31) - 1)
+    return fail(PKV_ERR_UNSUPPORTED, "rows or vocab beyond 2^31 - 1");
+  if (rows == 0) return ok();
+  if (!tokens || !logits || (!greedy && !gumbel)) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  pkv::SampleArgs a{};
+  a.logits = logits;
+  a.gumbel = gumbel;
+  a.tokens = tokens;
+  a.rows = rows;
+  a.vocab = vocab;
+  a.top_k = top_k;
+  a.inv_temperature = inv_t;
+  a.greedy = greedy ? 1 : 0;
+  return hip_status(pkv::launch_topk_sample(a, static_cast<hipStream_t>(stream)), "topk_sample launch");
+}
+
 pkv_status pkv_store_and_decode(void* out, const void* q, const void* k_new, const void* v_new,
                                 void* k_cache, void* v_cache, const int32_t* slot_mapping,
                                 const int32_t* block_tables, const int32_t* context_lens,

@@ -66,4 +66,17 @@ struct PrefillArgs {
 size_t prefill_workspace_bytes(int32_t num_seqs, int64_t total_q, int32_t group);
 hipError_t launch_varlen_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);
 
+// Temperature / top-k sampling of one token per row of logits.
+struct SampleArgs {
+  const float* logits;  // [rows, vocab]
+  const float* gumbel;  // [rows, vocab] standard Gumbel noise (read at the candidates)
+  int32_t* tokens;      // [rows]
+  int64_t rows, vocab;
+  int32_t top_k;        // <= 0 or >= vocab: no restriction
+  float inv_temperature;
+  int32_t greedy;       // temperature <= 0: first maximum of the logits
+};
+
+hipError_t launch_topk_sample(const SampleArgs& a, hipStream_t stream);
+
 }  // namespace pkv
