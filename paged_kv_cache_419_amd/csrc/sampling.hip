@@ -18,10 +18,16 @@
 // pattern mapped to an order-preserving unsigned key.  T <= 0 is greedy
 // (the first maximum of the logits).
 //
-// One workgroup of 1024 threads per row.  The k-th largest key is found by
-// three radix passes over the row (11, 11 and 10 bits, a 2048-bin histogram
-// in LDS each), a last pass evaluates the candidates; all passes read the
-// logits with coalesced loads.
+// One workgroup of 1024 threads per row.  Fast path (restricted top-k, large
+// vocabulary): a threshold below the k-th largest logit is estimated from
+// 1024 evenly spaced samples of the row, one pass over the row collects every
+// entry at or above it into LDS (wave-ballot compaction), and the exact k-th
+// largest and the draw are taken from those few entries (noise read at the
+// candidates only), so the row is read once.  When the estimate fails (fewer
+// than k or more than the LDS capacity collected: ties or odd distributions)
+// the general path runs: four radix passes over the row (8-bit digits, a
+// 256-bin LDS histogram each) find the k-th largest, and a last pass
+// evaluates the candidates.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,7 +36,8 @@ namespace pkv {
 namespace {
 
 constexpr int kSmThreads = 1024;
-constexpr int kSmBins = 2048;
+constexpr int kSmCap = 4096;       // entries the fast path can collect
+constexpr int kSmMinVocab = 8192;  // smaller rows take the general path
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -66,9 +73,57 @@ __device__ void block_best(float& v, int64_t& i, float* sv, int64_t* si) {
   __syncthreads();
 }
 
+// Radix selection of the k-th largest key among n keys given by key_at(i)
+// (0 <= i < n; every thread walks i = tid, tid + 1024, ...): four passes of
+// 8-bit digits, an LDS histogram of 256 bins each, scanned by one wave.
+// Requires 0 < k <= n.
+template <typename KeyAt>
+__device__ uint32_t kth_largest_key(KeyAt key_at, int64_t n, int k, int* hist, uint32_t* s_digit,
+                                    int* s_above) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  int remaining = k;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += kSmThreads) {
+      const uint32_t key = key_at(i);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l holds bins 4l .. 4l+3; suf = keys in the bins of lanes l .. 63
+      const int4 h = *reinterpret_cast<const int4*>(&hist[4 * tid]);
+      const int local = h.x + h.y + h.z + h.w;
+      int suf = local;
+      for (int off = 1; off < kWave; off <<= 1) {  // inclusive suffix scan over the lanes
+        const int v = __shfl_down(suf, off);
+        if (tid + off < kWave) suf += v;
+      }
+      const int above_lane = suf - local;  // keys whose digit is above this lane's bins
+      // number of keys with digit >= 4l + j, and with digit > 4l + j
+      const int ge[4] = {suf, above_lane + h.y + h.z + h.w, above_lane + h.z + h.w, above_lane + h.w};
+      const int gt[4] = {ge[1], ge[2], ge[3], above_lane};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (ge[j] >= remaining && gt[j] < remaining) {  // exactly one bin of the row
+          *s_digit = static_cast<uint32_t>(4 * tid + j);
+          *s_above = gt[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= *s_digit << shift;
+    mask |= 255u << shift;
+    remaining -= *s_above;
+    __syncthreads();
+  }
+  return prefix;
+}
+
 __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
-  __shared__ int hist[kSmBins];
-  __shared__ int suffix[kSmBins];
+  __shared__ __attribute__((aligned(16))) int hist[256];
   __shared__ float sv[kSmThreads / kWave];
   __shared__ int64_t si[kSmThreads / kWave];
   __shared__ uint32_t s_digit;
@@ -88,57 +143,97 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
     return;
   }
 
-  // k-th largest key: digits from the top, each pass among the keys that
-  // match the digits found so far.
-  uint32_t prefix = 0, mask = 0;
-  int remaining = a.top_k;
-  if (a.top_k > 0 && a.top_k < V) {
-    constexpr int kShift[3] = {21, 10, 0};
-    constexpr int kBits[3] = {11, 11, 10};
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const int shift = kShift[p];
-      const uint32_t nb = 1u << kBits[p];
-      for (int b = tid; b < kSmBins; b += kSmThreads) hist[b] = 0;
-      __syncthreads();
-      for (int64_t i = tid; i < V; i += kSmThreads) {
-        const uint32_t key = order_key(z[i]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
-      }
-      __syncthreads();
-      // suffix sums: suffix[b] = number of matching keys with digit >= b
-      for (int b = tid; b < kSmBins; b += kSmThreads) suffix[b] = b < static_cast<int>(nb) ? hist[b] : 0;
-      __syncthreads();
-      for (int d = 1; d < kSmBins; d <<= 1) {
-        int add[2] = {0, 0};
-        for (int j = 0; j < 2; ++j) {
-          const int b = tid + j * kSmThreads;
-          add[j] = b + d < kSmBins ? suffix[b + d] : 0;
-        }
-        __syncthreads();
-        for (int j = 0; j < 2; ++j) suffix[tid + j * kSmThreads] += add[j];
-        __syncthreads();
-      }
-      // the digit: the largest b with suffix[b] >= remaining (exactly one
-      // b has suffix[b] >= remaining > suffix[b + 1])
-      for (int j = 0; j < 2; ++j) {
-        const int b = tid + j * kSmThreads;
-        const int above = b + 1 < kSmBins ? suffix[b + 1] : 0;
-        if (b < static_cast<int>(nb) && suffix[b] >= remaining && above < remaining) {
-          s_digit = static_cast<uint32_t>(b);
-          s_above = above;
-        }
-      }
-      __syncthreads();
-      prefix |= s_digit << shift;
-      mask |= (nb - 1) << shift;
-      remaining -= s_above;
-      __syncthreads();
-    }
-  }
-  const uint32_t tau = prefix;  // 0 (every key) when top_k does not restrict
-
   const float* g = a.gumbel + row * V;
+  const bool restricted = a.top_k > 0 && a.top_k < V;
+
+  if (restricted && V >= kSmMinVocab) {
+    // Fast path.  Threshold: the s-th largest of 1024 evenly spaced samples,
+    // s chosen so that about 4 k entries of the row (at least 4 samples' worth)
+    // lie above it: enough to hold the top k, few enough for the LDS.  (A row
+    // where this fails is only slower: it takes the general path.)
+    __shared__ uint32_t ckey[kSmCap];
+    __shared__ int cidx[kSmCap];
+    __shared__ uint32_t skey[kSmThreads];
+    __shared__ int s_count;
+    const int64_t sidx = (static_cast<int64_t>(tid) * V) / kSmThreads;
+    skey[tid] = order_key(z[sidx]);
+    if (tid == 0) s_count = 0;
+    const int64_t want = (static_cast<int64_t>(kSmThreads) * 4 * a.top_k + V - 1) / V + 4;
+    const int s_rank = static_cast<int>(min<int64_t>(want, kSmThreads));
+    __syncthreads();
+    // (every thread gets the same key back)
+    const uint32_t tau0 = kth_largest_key([&](int64_t i) { return skey[i]; }, kSmThreads, s_rank, hist,
+                                          &s_digit, &s_above);
+    // Collect every entry with key >= tau0 (one wave-wide reservation per
+    // step; entries past the capacity are counted, not stored).
+    const int lane = tid & (kWave - 1);
+    auto push = [&](bool take, uint32_t key, int64_t idx) {
+      const uint64_t m = __ballot(take);
+      if (m == 0) return;
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_count, __popcll(m));
+      base = __shfl(base, 0);
+      const int pos = base + __popcll(m & ((1ull << lane) - 1));
+      if (take && pos < kSmCap) {
+        ckey[pos] = key;
+        cidx[pos] = static_cast<int>(idx);
+      }
+    };
+    const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
+    if (vec) {
+      // kSmUnroll 16-byte loads per thread in flight, then their entries
+      constexpr int kSmUnroll = 8;
+      const float4* z4 = reinterpret_cast<const float4*>(z);
+      const int64_t n4 = V / 4;
+      for (int64_t i0 = tid; i0 - tid < n4; i0 += kSmUnroll * kSmThreads) {
+        float4 v[kSmUnroll];
+#pragma unroll
+        for (int u = 0; u < kSmUnroll; ++u) {
+          const int64_t i = i0 + u * kSmThreads;
+          v[u] = i < n4 ? z4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kSmUnroll; ++u) {
+          const int64_t i = i0 + u * kSmThreads;
+          const bool live = i < n4;
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t key = order_key(e[c]);
+            push(live && key >= tau0, key, 4 * i + c);
+          }
+        }
+      }
+    } else {
+      for (int64_t i = tid; i - tid < V; i += kSmThreads) {
+        const bool live = i < V;
+        const uint32_t key = live ? order_key(z[i]) : 0u;
+        push(live && key >= tau0, key, i);
+      }
+    }
+    __syncthreads();
+    const int count = s_count;
+    if (count >= a.top_k && count <= kSmCap) {
+      const uint32_t tau = kth_largest_key([&](int64_t i) { return ckey[i]; }, count, a.top_k, hist,
+                                           &s_digit, &s_above);
+      for (int j = tid; j < count; j += kSmThreads) {
+        if (ckey[j] >= tau) {
+          const int64_t i = cidx[j];
+          keep_best(best, best_i, __fadd_rn(__fmul_rn(z[i], a.inv_temperature), g[i]), i);
+        }
+      }
+      block_best(best, best_i, sv, si);
+      if (tid == 0) a.tokens[row] = static_cast<int32_t>(best_i);
+      return;
+    }
+    __syncthreads();  // the LDS scratch is reused below
+  }
+
+  // General path: the k-th largest key by radix passes over the row.
+  const uint32_t tau = restricted
+      ? kth_largest_key([&](int64_t i) { return order_key(z[i]); }, V, a.top_k, hist, &s_digit,
+                        &s_above)
+      : 0u;  // every key
   for (int64_t i = tid; i < V; i += kSmThreads) {
     const float zi = z[i];
     if (order_key(zi) >= tau) keep_best(best, best_i, __fadd_rn(__fmul_rn(zi, a.inv_temperature), g[i]), i);
