@@ -10,9 +10,10 @@ rotated between steps so that a step does not find the previous step's K/V in
 L2 or the Infinity Cache.
 
 Prints one JSON line: whole-step throughput (algorithmic HBM bytes per second
-for decode, algorithmic FLOP/s for prefill), a roofline object for the
-attention kernel timed with HIP events around each launch inside the timed
-region, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+for decode, algorithmic FLOP/s for prefill) over K steps between two HIP
+events, a roofline object for the attention call (its average launch duration
+from K back-to-back launches between two HIP events on the launch stream), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -70,6 +71,7 @@ CALL_SOURCES = {
     "paged_decode_attention": ("paged_decode.hip",),
     "varlen_prefill_attention": ("varlen_prefill.hip",),
     "store_kvcache": ("store_kvcache.hip",),
+    "topk_sample": ("sampling.hip",),
 }
 SHARED_SOURCES = ("common.h", "kernels.h")
 
@@ -89,6 +91,7 @@ CALL_KERNELS = {
     "paged_decode_attention": ("paged_decode_kernel", "paged_decode_combine_kernel"),
     "varlen_prefill_attention": ("varlen_prefill_kernel", "prefill_plan_kernel"),
     "store_kvcache": ("store_kvcache_kernel",),
+    "topk_sample": ("topk_sample_kernel",),
 }
 COPY_PROBE_BYTES = 1 << 30  # plain device-to-device copy that calibrates the counters
 COPY_KERNEL = "copyBuffer"
@@ -107,6 +110,16 @@ def measured_traffic(workload: str, call: str):
     if rec.get("kernel_sources_sha") != kernel_sources_sha(call):
         return None
     return rec.get("hbm_bytes_per_call")
+
+
+def copy_probe(torch, dev):
+    """The 1 GiB device copy that calibrates FETCH_SIZE and WRITE_SIZE (three dispatches)."""
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def _counter_values(run_dir: str, counter: str):
@@ -235,14 +248,15 @@ def run_sampling(args, torch, pkv, dev):
         pkv.topk_sample(tok[i % reps], lg[i % reps], gg[i % reps], SAMPLE_TOP_K, SAMPLE_TEMPERATURE)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):  # the step is this one kernel, launched back to back
         pkv.topk_sample(tok[i % reps], lg[i % reps], gg[i % reps], SAMPLE_TOP_K, SAMPLE_TEMPERATURE)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    ms = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
-    call_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    call_ms = ms
     import oracle.sampling as OS
     want = OS.topk_sample(logits, gumbel, SAMPLE_TOP_K, SAMPLE_TEMPERATURE)
     assert np.array_equal(tok[0].cpu().numpy(), want), "sampled tokens differ from the oracle"
@@ -257,7 +271,8 @@ def run_sampling(args, torch, pkv, dev):
                    "top_k": SAMPLE_TOP_K, "temperature": SAMPLE_TEMPERATURE,
                    "input_copies_rotated": reps, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "topk_sample",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(SAMPLE_WORKLOAD, "topk_sample"), "kernel": "topk_sample",
                      "kernel_ms": call_ms},
         "rows_per_s": SAMPLE_ROWS / (ms * 1e-3),
     }
@@ -271,6 +286,8 @@ def run_sampling(args, torch, pkv, dev):
         rec["cpu_baseline"] = {"value": n * (nbytes / SAMPLE_ROWS) / dt / 1e9, "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
                                "sample": f"{n} of {SAMPLE_ROWS} rows (NumPy, one thread), {dt:.1f} s"}
+    if args.copy_probe:
+        copy_probe(torch, dev)
     print(json.dumps(rec), flush=True)
 
 
@@ -349,20 +366,28 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        c = copies[i % reps]
-        ev[i][0].record(stream)
-        store(c)
-        ev[i][1].record(stream)
-        attend(c, outs[i % reps])
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev[0][0].elapsed_time(ev[-1][2])
-    store_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    ms_step = total_ms / args.steps
+
+    def timed(body) -> float:
+        """Average ms per iteration of `body(i)` over the K steps, launched back to back."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            body(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def step(i):
+        store(copies[i % reps])
+        attend(copies[i % reps], outs[i % reps])
+
+    # the timed region: K whole steps (store + attention); then each call's own
+    # launch duration, from K back-to-back launches of that call alone
+    ms_step = timed(step)
+    attn_ms = timed(lambda i: attend(copies[i % reps], outs[i % reps]))
+    store_ms = timed(lambda i: store(copies[i % reps]))
 
     if decode:
         step_bytes = decode_bytes(w) + store_bytes(w)
@@ -452,12 +477,7 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     if args.copy_probe:
-        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(torch, dev)
     print(json.dumps(rec), flush=True)
 
 

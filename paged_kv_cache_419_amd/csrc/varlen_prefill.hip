@@ -47,8 +47,8 @@ constexpr int kPfKB = kPfKeys / 32;  // 32-key MFMA blocks per tile
 constexpr int kPfU = kPfKeys / 16;   // 16-key k-blocks of the PV product per tile
 constexpr int kPfRows = 32;  // query rows per wave (the N side of a 32x32 MFMA)
 constexpr float kRescaleSlack = 8.f;  // log2 headroom of the lazy softmax rescale
-constexpr unsigned short kSlackBf16Bits = 0x4380;  // bf16 bit pattern of 2^kRescaleSlack
-static_assert(kSlackBf16Bits == (127 + static_cast<int>(kRescaleSlack)) << 7, "bf16 of 2^slack");
+constexpr float kSlackSum = 256.f;    // 2^kRescaleSlack
+static_assert(kSlackSum == (1 << static_cast<int>(kRescaleSlack)), "2^slack");
 
 template <int D>
 struct PrefillShape {
@@ -201,45 +201,48 @@ __device__ __forceinline__ void sched_reads_ahead() {
 // Weights exp2(s c - m) of one 64-key tile, rounded to bf16 and packed in
 // the B-operand order of the PV product: 16-key block u = 2 kb + hb, k-slots
 // 0..3 are keys 16u + 4h + i, k-slots 4..7 are keys 16u + 8 + 4h + i.
-// Returns the sum of this lane's 32 weights (fp32, before rounding).
+// Returns the fp32 sum of this lane's 32 weights as rounded (the weights the
+// PV product uses), taken two at a time by packed bf16 dot products with 1.
+// (The dot product takes the bf16 pairs as built, not bit-cast back out of
+// the packed words: hipcc 7.2 miscompiles the latter, reusing element 0.)
 __device__ __forceinline__ float tile_weights(const f32x16 (&s)[kPfKB], u32x4 (&pb)[kPfU], float m, float c) {
-  float sum = 0.f;
+  const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  float sum[2] = {0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < kPfKB; ++kb) {
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = fast_exp2(__builtin_fmaf(s[kb][v], c, -m));
-    float part[4];
+    bf16x2 b[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) part[j] = (p[4 * j] + p[4 * j + 1]) + (p[4 * j + 2] + p[4 * j + 3]);
-    sum += (part[0] + part[1]) + (part[2] + part[3]);
+    for (int e = 0; e < 8; ++e) {
+      b[e] = bf16x2{static_cast<__bf16>(p[2 * e]), static_cast<__bf16>(p[2 * e + 1])};
+      sum[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(b[e], one, sum[e & 1], false);
+    }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int j = 2 * hb;
-      pb[2 * kb + hb] = u32x4{pack_bf16x2(p[4 * j], p[4 * j + 1]), pack_bf16x2(p[4 * j + 2], p[4 * j + 3]),
-                              pack_bf16x2(p[4 * j + 4], p[4 * j + 5]),
-                              pack_bf16x2(p[4 * j + 6], p[4 * j + 7])};
+      auto w = [&](int e) { return __builtin_bit_cast(uint32_t, b[4 * hb + e]); };
+      pb[2 * kb + hb] = u32x4{w(0), w(1), w(2), w(3)};
     }
   }
-  return sum;
+  return sum[0] + sum[1];
 }
 
-// True when some packed bf16 weight is >= 2^kRescaleSlack (or inf / NaN):
-// weights are non-negative, so their bit patterns order like their values;
-// a packed 16-bit max folds two weights per instruction.
-__device__ __forceinline__ bool weights_overflow(const u32x4 (&pb)[kPfU]) {
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  u16x2 mx = __builtin_bit_cast(u16x2, pb[0][0]);
+// Largest s c over this lane's row (both lanes of the row: lane and lane ^ 32).
+// c may be negative: the largest s c is then c times the smallest s.  Masked
+// scores are -inf for c > 0 and +inf for c < 0, so they never win.
+__device__ __forceinline__ float row_max_scaled(const f32x16 (&s)[kPfKB], float c) {
+  float mx = s[0][0], mn = s[0][0];
 #pragma unroll
-  for (int u = 0; u < kPfU; ++u)
+  for (int kb = 0; kb < kPfKB; ++kb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (u != 0 || e != 0) {
-        const u16x2 v = __builtin_bit_cast(u16x2, pb[u][e]);
-        mx = __builtin_elementwise_max(mx, v);
-      }
-  const unsigned short lim = kSlackBf16Bits;
-  return (mx[0] >= lim) || (mx[1] >= lim);
+    for (int v = 0; v < 16; ++v) {
+      mx = fmaxf(mx, s[kb][v]);
+      mn = fminf(mn, s[kb][v]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mn = fminf(mn, __shfl_xor(mn, 32));
+  return c > 0.f ? mx * c : mn * c;
 }
 
 // One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
@@ -251,7 +254,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
                                              const uint32_t (&kaddr)[PrefillShape<D>::KS],
                                              const uint32_t (&vaddr)[PrefillShape<D>::DC],
                                              int k0, int lim, bool need_mask, int h,
-                                             float c, float sgn, const DmaJob& job,
+                                             float c, float masked, const DmaJob& job,
                                              const TileLoadOffsets<D>& lo) {
   using S = PrefillShape<D>;
   constexpr int kGap = kPfKB * S::KS / (2 * S::LOADS);
@@ -277,35 +280,21 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
     for (int kb = 0; kb < kPfKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        if (k0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3) > lim) s[kb][v] = -INFINITY * sgn;
+        if (k0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3) > lim) s[kb][v] = masked;
   }
   // Weights p = exp2(s c - m) against the running reference m.  m only has
   // to bound the scores loosely: the weights are consistent with the sums and
   // O whatever m is.  It is first set from the first tile's max; afterwards
-  // the max is not computed at all: the tile's weights are checked instead,
-  // and only when some weight reaches 2^kRescaleSlack (its row's max rose by
-  // that much, rare after the first tiles) is m raised and O rescaled.
-  // c may be negative (sgn = -1): masked scores are then +inf, and the
-  // largest s c of a row is |c| times the largest s sgn.
-  if (__ballot(w.m == -INFINITY) != 0) {  // first tile of this wave
-    float mx = s[0][0] * sgn;
-#pragma unroll
-    for (int kb = 0; kb < kPfKB; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v] * sgn);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    w.m = mx * (c * sgn);
-  }
+  // the max is not computed at all: the tile's weight sums are checked
+  // instead, and only when a lane's sum reaches 2^kRescaleSlack (so possibly
+  // one of its weights did: its row's max rose by up to that much, rare after
+  // the first tiles; inf and NaN also fail the check) is m raised to the
+  // tile's max and O rescaled.
+  if (__ballot(w.m == -INFINITY) != 0) w.m = row_max_scaled(s, c);  // first tile of this wave
   u32x4 pb[kPfU];
   float tsum = tile_weights(s, pb, w.m, c);
-  if (__ballot(weights_overflow(pb)) != 0) {
-    float mx = s[0][0] * sgn;
-#pragma unroll
-    for (int kb = 0; kb < kPfKB; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v] * sgn);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(w.m, mx * (c * sgn));
+  if (__ballot(!(tsum < kSlackSum)) != 0) {
+    const float m_new = fmaxf(w.m, row_max_scaled(s, c));
     const float alpha = fast_exp2(w.m - m_new);
     w.lsum *= alpha;
 #pragma unroll
@@ -554,7 +543,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
   // a tiny one: every visible key then gets weight 1, and masked keys (score
   // -inf) still get 0.
   const float c = a.scale_log2 != 0.f ? a.scale_log2 : 1e-30f;
-  const float sgn = c > 0.f ? 1.f : -1.f;
+  const float masked = c > 0.f ? -INFINITY : INFINITY;  // score of a masked key: weight 0
   const uint32_t row_bytes = static_cast<uint32_t>(a.num_kv_heads) * D * 2;
   const TileLoadOffsets<D> lo = tile_load_offsets<D>(lane, wave, row_bytes);
 
@@ -682,7 +671,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
     for (; t < min(n_compute, n_inner); ++t, ++T) {
       const DmaJob job = inner_step(t);
       const int k0 = t * kPfKeys;
-      compute_tile<D>(w, kslot(T), vslot(T), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c, sgn, job, lo);
+      compute_tile<D>(w, kslot(T), vslot(T), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c, masked, job, lo);
     }
 #pragma unroll 1
     for (; t < n_inner; ++t, ++T) dma_all<D>(inner_step(t), lo);
@@ -708,7 +697,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
     if (threadIdx.x == 0) ticket = after >= 0 ? atomicAdd(&counters[xcc * kQueueStride], 1) : -2;
     if (t < n_compute) {
       const int k0 = t * kPfKeys;
-      compute_tile<D>(w, kslot(T), vslot(T), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c, sgn, job, lo);
+      compute_tile<D>(w, kslot(T), vslot(T), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c, masked, job, lo);
     } else {
       dma_all<D>(job, lo);
     }

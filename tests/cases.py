@@ -57,6 +57,14 @@ def small_workloads():
     cases["decode_negscale"] = W.decode([3, 40, 257], num_q_heads=8, num_kv_heads=4,
                                         head_dim=128, block_size=16, seed=22, scale=-0.5,
                                         name="decode_negscale")
+    # a large scale: the scaled scores spread over tens of log2 units, so rows meet keys far
+    # above the first tile's maximum and the kernels' lazy rescale of the running max runs
+    cases["prefill_bigscale"] = W.prefill([190, 64, 129], hist=[0, 100, 0], num_q_heads=4,
+                                          num_kv_heads=1, head_dim=128, block_size=32, seed=23,
+                                          scale=3.0, name="prefill_bigscale")
+    cases["decode_bigscale"] = W.decode([190, 700, 5], num_q_heads=4, num_kv_heads=2,
+                                        head_dim=128, block_size=16, seed=24, scale=3.0,
+                                        name="decode_bigscale")
     return cases
 
 
