@@ -728,8 +728,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
     }
     if (!has_next) break;
     cur = nx;
+    // The next item's Q rows take over here, after the output stores: the
+    // empty asm keeps the compiler from moving the hand-over (and so its
+    // wait for the Q loads, which would also wait for the next tile's loads
+    // issued after them) to the start of the epilogue.
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) w.qb[ks] = qn[ks];
+    for (int ks = 0; ks < S::KS; ++ks) {
+      asm volatile("" : "+v"(qn[ks]));
+      w.qb[ks] = qn[ks];
+    }
     nxt_id = after;
   }
   // The last ring step's loads (zero fills) and the output stores must be
