@@ -20,8 +20,9 @@
 //
 // One workgroup of 1024 threads per row.  Fast path (restricted top-k, large
 // vocabulary): a threshold below the k-th largest logit is estimated from
-// 1024 evenly spaced samples of the row, one pass over the row collects every
-// entry at or above it into LDS (wave-ballot compaction), and the exact k-th
+// 1024 samples of the row, 64 evenly spaced runs of 16 entries (while the
+// first part of the row is already streaming in), one pass over the row collects every entry at or
+// above it into LDS (wave-ballot compaction), and the exact k-th
 // largest and the draw are taken from those few entries (noise read at the
 // candidates only), so the row is read once.  When the estimate fails (fewer
 // than k or more than the LDS capacity collected: ties or odd distributions)
@@ -75,27 +76,47 @@ __device__ void block_best(float& v, int64_t& i, float* sv, int64_t* si) {
 
 // Radix selection of the k-th largest key among n keys given by key_at(i)
 // (0 <= i < n; every thread walks i = tid, tid + 1024, ...): four passes of
-// 8-bit digits, an LDS histogram of 256 bins each, scanned by one wave.
-// Requires 0 < k <= n.
+// 8-bit digits, each with its own 256-bin LDS histogram (hist: 4 x 256 ints,
+// all cleared up front), scanned by one wave; two barriers per pass.  Keys
+// often share their high digits (samples of a row do, and the candidates
+// above a threshold all do), so each wave first adds up the lanes that share
+// the digit of its first active lane and commits them with one atomic; the
+// other lanes add one each.  Requires 0 < k <= n.
 template <typename KeyAt>
 __device__ uint32_t kth_largest_key(KeyAt key_at, int64_t n, int k, int* hist, uint32_t* s_digit,
                                     int* s_above) {
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  static_assert(kSmThreads == 4 * 256, "one histogram word per thread to clear");
+  hist[tid] = 0;
+  __syncthreads();
   uint32_t prefix = 0, mask = 0;
   int remaining = k;
 #pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    int* h = hist + 256 * pass;
     for (int64_t i = tid; i < n; i += kSmThreads) {
       const uint32_t key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      const bool act = (key & mask) == prefix;
+      const uint32_t d = (key >> shift) & 255;
+      const uint64_t am = __ballot(act);
+      if (am != 0) {
+        const int leader = static_cast<int>(__builtin_ctzll(am));
+        const uint32_t ld = static_cast<uint32_t>(__shfl(static_cast<int>(d), leader));
+        const uint64_t same = __ballot(act && d == ld);
+        if (lane == leader) {
+          atomicAdd(&h[ld], static_cast<int>(__popcll(same)));
+        } else if (act && d != ld) {
+          atomicAdd(&h[d], 1);
+        }
+      }
     }
     __syncthreads();
     if (tid < kWave) {
       // lane l holds bins 4l .. 4l+3; suf = keys in the bins of lanes l .. 63
-      const int4 h = *reinterpret_cast<const int4*>(&hist[4 * tid]);
-      const int local = h.x + h.y + h.z + h.w;
+      const int4 hv = *reinterpret_cast<const int4*>(&h[4 * tid]);
+      const int local = hv.x + hv.y + hv.z + hv.w;
       int suf = local;
       for (int off = 1; off < kWave; off <<= 1) {  // inclusive suffix scan over the lanes
         const int v = __shfl_down(suf, off);
@@ -103,31 +124,31 @@ __device__ uint32_t kth_largest_key(KeyAt key_at, int64_t n, int k, int* hist, u
       }
       const int above_lane = suf - local;  // keys whose digit is above this lane's bins
       // number of keys with digit >= 4l + j, and with digit > 4l + j
-      const int ge[4] = {suf, above_lane + h.y + h.z + h.w, above_lane + h.z + h.w, above_lane + h.w};
+      const int ge[4] = {suf, above_lane + hv.y + hv.z + hv.w, above_lane + hv.z + hv.w, above_lane + hv.w};
       const int gt[4] = {ge[1], ge[2], ge[3], above_lane};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (ge[j] >= remaining && gt[j] < remaining) {  // exactly one bin of the row
-          *s_digit = static_cast<uint32_t>(4 * tid + j);
-          *s_above = gt[j];
+          s_digit[pass] = static_cast<uint32_t>(4 * tid + j);
+          s_above[pass] = gt[j];
         }
       }
     }
     __syncthreads();
-    prefix |= *s_digit << shift;
+    prefix |= s_digit[pass] << shift;
     mask |= 255u << shift;
-    remaining -= *s_above;
-    __syncthreads();
+    remaining -= s_above[pass];
   }
+  // (the caller may reuse hist, s_digit and s_above only after a barrier)
   return prefix;
 }
 
 __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
-  __shared__ __attribute__((aligned(16))) int hist[256];
+  __shared__ __attribute__((aligned(16))) int hist[4 * 256];
   __shared__ float sv[kSmThreads / kWave];
   __shared__ int64_t si[kSmThreads / kWave];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_above;
+  __shared__ uint32_t s_digit[4];
+  __shared__ int s_above[4];
 
   const int64_t row = blockIdx.x;
   const int64_t V = a.vocab;
@@ -147,7 +168,7 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
   const bool restricted = a.top_k > 0 && a.top_k < V;
 
   if (restricted && V >= kSmMinVocab) {
-    // Fast path.  Threshold: the s-th largest of 1024 evenly spaced samples,
+    // Fast path.  Threshold: the s-th largest of 1024 samples of the row,
     // s chosen so that about 4 k entries of the row (at least 4 samples' worth)
     // lie above it: enough to hold the top k, few enough for the LDS.  (A row
     // where this fails is only slower: it takes the general path.)
@@ -155,15 +176,45 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
     __shared__ int cidx[kSmCap];
     __shared__ uint32_t skey[kSmThreads];
     __shared__ int s_count;
-    const int64_t sidx = (static_cast<int64_t>(tid) * V) / kSmThreads;
-    skey[tid] = order_key(z[sidx]);
+    // The collect pass's first loads go out now, so that the row streams in
+    // while the threshold is selected (kSmUnroll 16-byte loads per thread in
+    // flight, 128 KiB per row).
+    constexpr int kSmUnroll = 8;
+    // 1024 samples in 64 evenly spaced runs of 16 consecutive entries: 64
+    // cache lines per row (1024 lone entries would fetch 1024 lines)
+    const int64_t sidx = static_cast<int64_t>(tid >> 4) * (V >> 6) + (tid & 15);
+    // The sample is loaded first and waited for by count (the batch's
+    // kSmUnroll loads may stay in flight): the load and its wait are written
+    // out, because the compiler would wait for every load before the first
+    // use of the sample.
+    float zs;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(zs) : "v"(z + sidx) : "memory");
+    // Every wave's sample load goes out before any wave's batch loads (a
+    // bare barrier: it orders the issue and waits for no memory), so the
+    // samples do not queue behind 128 KiB of row data.
+    __builtin_amdgcn_s_barrier();
+    const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    const int64_t n4 = V / 4;
+    // (indices past the row are clamped to its last entry: the loads stay
+    // unconditional, and the collect pass skips those entries)
+    float4 first[kSmUnroll];
+    static_assert(kSmUnroll == 8, "the wait below counts kSmUnroll loads");
+    if (vec) {
+#pragma unroll
+      for (int u = 0; u < kSmUnroll; ++u) first[u] = z4[min(tid + static_cast<int64_t>(u) * kSmThreads, n4 - 1)];
+      asm volatile("s_waitcnt vmcnt(8)" : "+v"(zs) : : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(zs) : : "memory");
+    }
+    skey[tid] = order_key(zs);
     if (tid == 0) s_count = 0;
     const int64_t want = (static_cast<int64_t>(kSmThreads) * 4 * a.top_k + V - 1) / V + 4;
     const int s_rank = static_cast<int>(min<int64_t>(want, kSmThreads));
     __syncthreads();
     // (every thread gets the same key back)
     const uint32_t tau0 = kth_largest_key([&](int64_t i) { return skey[i]; }, kSmThreads, s_rank, hist,
-                                          &s_digit, &s_above);
+                                          s_digit, s_above);
     // Collect every entry with key >= tau0 (one wave-wide reservation per
     // step; entries past the capacity are counted, not stored).
     const int lane = tid & (kWave - 1);
@@ -179,19 +230,14 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
         cidx[pos] = static_cast<int>(idx);
       }
     };
-    const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
     if (vec) {
+      // The float tf whose key is tau0: !(f < tf) holds for every f with
+      // key >= tau0 (also NaN, and -0 against +0, which the exact test then
+      // drops), so one float compare per entry finds the few entries that
+      // need the exact test.
+      const float tf = __uint_as_float((tau0 & 0x80000000u) ? (tau0 & 0x7FFFFFFFu) : ~tau0);
       // kSmUnroll 16-byte loads per thread in flight, then their entries
-      constexpr int kSmUnroll = 8;
-      const float4* z4 = reinterpret_cast<const float4*>(z);
-      const int64_t n4 = V / 4;
-      for (int64_t i0 = tid; i0 - tid < n4; i0 += kSmUnroll * kSmThreads) {
-        float4 v[kSmUnroll];
-#pragma unroll
-        for (int u = 0; u < kSmUnroll; ++u) {
-          const int64_t i = i0 + u * kSmThreads;
-          v[u] = i < n4 ? z4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+      auto collect = [&](const float4 (&v)[kSmUnroll], int64_t i0) {
 #pragma unroll
         for (int u = 0; u < kSmUnroll; ++u) {
           const int64_t i = i0 + u * kSmThreads;
@@ -199,10 +245,22 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
           const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const uint32_t key = order_key(e[c]);
-            push(live && key >= tau0, key, 4 * i + c);
+            const bool maybe = live && !(e[c] < tf);
+            if (__ballot(maybe) != 0) {
+              const uint32_t key = order_key(e[c]);
+              push(maybe && key >= tau0, key, 4 * i + c);
+            }
           }
         }
+      };
+      collect(first, tid);
+      for (int64_t i0 = tid + kSmUnroll * kSmThreads; i0 - tid < n4; i0 += kSmUnroll * kSmThreads) {
+        float4 v[kSmUnroll];
+#pragma unroll
+        for (int u = 0; u < kSmUnroll; ++u) v[u] = z4[min(i0 + u * kSmThreads, n4 - 1)];
+        // all kSmUnroll loads go out before the first entry is looked at
+        __builtin_amdgcn_sched_barrier(0);
+        collect(v, i0);
       }
     } else {
       for (int64_t i = tid; i - tid < V; i += kSmThreads) {
@@ -215,7 +273,7 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
     const int count = s_count;
     if (count >= a.top_k && count <= kSmCap) {
       const uint32_t tau = kth_largest_key([&](int64_t i) { return ckey[i]; }, count, a.top_k, hist,
-                                           &s_digit, &s_above);
+                                           s_digit, s_above);
       for (int j = tid; j < count; j += kSmThreads) {
         if (ckey[j] >= tau) {
           const int64_t i = cidx[j];
@@ -231,8 +289,7 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
 
   // General path: the k-th largest key by radix passes over the row.
   const uint32_t tau = restricted
-      ? kth_largest_key([&](int64_t i) { return order_key(z[i]); }, V, a.top_k, hist, &s_digit,
-                        &s_above)
+      ? kth_largest_key([&](int64_t i) { return order_key(z[i]); }, V, a.top_k, hist, s_digit, s_above)
       : 0u;  // every key
   for (int64_t i = tid; i < V; i += kSmThreads) {
     const float zi = z[i];
