@@ -65,6 +65,22 @@ def small_workloads():
     cases["decode_bigscale"] = W.decode([190, 700, 5], num_q_heads=4, num_kv_heads=2,
                                         head_dim=128, block_size=16, seed=24, scale=3.0,
                                         name="decode_bigscale")
+    # batches whose (sequence, kv head) items outnumber the resident workgroups several
+    # times over: many equal contexts, empty contexts, head groups of 16 with two groups
+    # per kv head, and batches of 512 and 513 sequences
+    rng = np.random.Generator(np.random.PCG64(25))
+    cases["decode_many_b300"] = W.decode(
+        rng.choice([0, 1, 2, 37, 64, 100, 129, 160], size=300).tolist(), num_q_heads=8,
+        num_kv_heads=4, head_dim=64, block_size=32, seed=25, name="decode_many_b300")
+    cases["decode_many_g32"] = W.decode(
+        rng.integers(0, 80, size=260, endpoint=True).tolist(), num_q_heads=32, num_kv_heads=1,
+        head_dim=64, block_size=16, seed=26, name="decode_many_g32")
+    cases["decode_many_b512"] = W.decode(
+        rng.integers(1, 40, size=512, endpoint=True).tolist(), num_q_heads=16, num_kv_heads=8,
+        head_dim=128, block_size=32, seed=27, name="decode_many_b512")
+    cases["decode_b513"] = W.decode(
+        rng.integers(1, 20, size=513, endpoint=True).tolist(), num_q_heads=1, num_kv_heads=1,
+        head_dim=64, block_size=16, seed=28, name="decode_b513")
     return cases
 
 
