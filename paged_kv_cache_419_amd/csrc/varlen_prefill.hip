@@ -358,11 +358,11 @@ __device__ __forceinline__ void tile_sync_and_issue(const SeqView& sv, int t, in
 // kernel lists the (sequence, q tile) pairs that hold at least one query row,
 // sequence by sequence and latest q tile first, as records carrying what a
 // workgroup needs to start on the pair; item i is pair i / ipp, kv head
-// (i % ipp) / head_groups, head group i % head_groups (ipp = Hkv *
-// head_groups).  Items are dealt to eight queues, item i to queue i % 8, one
-// queue per XCD: a workgroup takes items from the queue of the XCD it runs on
-// (its hardware XCC id), so with 8 | Hkv each XCD serves one kv head and the
-// K/V it streams stay in its own L2.  A queue is a counter in the workspace
+// (i % ipp) % Hkv, head group (i % ipp) / Hkv (ipp = Hkv * head_groups).
+// Items are dealt to eight queues, item i to queue i % 8, one queue per XCD:
+// a workgroup takes items from the queue of the XCD it runs on (its hardware
+// XCC id), so with 8 | Hkv each XCD serves one kv head, whatever the number
+// of head groups, and the K/V it streams stay in its own L2.  A queue is a counter in the workspace
 // bumped by one atomic per item; once its own queue is drained a workgroup
 // takes items from the others.
 //
@@ -485,8 +485,9 @@ __device__ __forceinline__ Item item_of(const PrefillSched& sc, int id, const u3
                                         int ipp) {
   Item it;
   const int rem = id % ipp;
-  it.g = rem / sc.head_groups;
-  it.hg = rem % sc.head_groups;
+  const int hkv = ipp / sc.head_groups;
+  it.g = rem % hkv;
+  it.hg = rem / hkv;
   auto f = [&](int i) { return __builtin_amdgcn_readfirstlane(static_cast<int>(r[i >> 2][i & 3])); };
   it.seq = f(kRecSeq);
   it.qtile = f(kRecQtile);
