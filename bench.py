@@ -240,7 +240,10 @@ def sample_bytes(logits: np.ndarray, top_k: int) -> int:
 def run_sampling(args, torch, pkv, dev):
     from workload.sample import SAMPLE_ROWS, SAMPLE_TEMPERATURE, SAMPLE_TOP_K, SAMPLE_VOCAB, sample_inputs
     logits, gumbel = sample_inputs(SAMPLE_ROWS, SAMPLE_VOCAB, seed=4196)
-    reps = args.replicas or 2  # 2 x 311 MB: no step finds its rows in the Infinity Cache
+    # 4 x 311 MB: between two uses of one copy the other three copies' 466 MB of logits
+    # are read, more than the 256 MB Infinity Cache holds (with 2 copies, 155 MB in
+    # between, a call ran ~3 % faster: some rows were still cached)
+    reps = args.replicas or 4
     lg = [torch.from_numpy(logits).to(dev) for _ in range(reps)]
     gg = [torch.from_numpy(gumbel).to(dev) for _ in range(reps)]
     tok = [torch.empty(SAMPLE_ROWS, dtype=torch.int32, device=dev) for _ in range(reps)]
