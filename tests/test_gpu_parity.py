@@ -107,6 +107,37 @@ def test_deterministic_and_block_permutation(name):
 
 
 # ---- the five workloads at full size, as the benchmark launches them ----------------
+def _within_visible_v_range(w, t, out):
+    """Every row, at any size: an attention output is a convex combination of the V rows
+    its query sees (softmax weights are non-negative and sum to one), so each element lies
+    between the least and the greatest value of its column over those rows.  Checked for
+    every output row, within the attention tolerance."""
+    g = w.num_q_heads // w.num_kv_heads
+    vc = t["v_cache"]
+    of = out.float()
+    dev = vc.device
+    for s in range(w.num_seqs):
+        lk, lq = int(w.lk[s]), int(w.lq[s])
+        if w.kind == "decode" and lk == 0:  # an empty context gives a zero row
+            assert not bool(of[s].any()), f"sequence {s}: empty context, nonzero output"
+            continue
+        if lq == 0:
+            continue
+        slots = torch.from_numpy(w.slots(s, np.arange(lk))).to(dev)
+        v = vc[slots].float()  # [lk, Hkv, d]
+        o = of[torch.from_numpy(H.rows_for(w, [s])).to(dev)]  # [rows, Hq, d]
+        if w.kind == "decode":
+            lo, hi = v.amin(0, keepdim=True), v.amax(0, keepdim=True)
+        else:  # row r sees keys 0 .. lk - lq + r (all lk keys without the causal mask)
+            last = (lk - lq + torch.arange(lq, device=dev)) if w.causal else torch.full((lq,), lk - 1, device=dev)
+            lo = torch.cummin(v, 0).values[last]
+            hi = torch.cummax(v, 0).values[last]
+        lo = lo.repeat_interleave(g, dim=1)
+        hi = hi.repeat_interleave(g, dim=1)
+        bad = (o < lo - (1e-2 + 1e-2 * lo.abs())) | (o > hi + (1e-2 + 1e-2 * hi.abs()))
+        assert not bool(bad.any()), f"sequence {s}: {int(bad.sum())} outputs outside the range of the V rows they see"
+
+
 def _samples(w, k):
     lens = w.lk if w.kind == "decode" else w.lq
     rng = np.random.Generator(np.random.PCG64(11))
@@ -142,3 +173,5 @@ def test_full_size(name, k):
     ea, er = H.check_against_oracle(w, out, seqs)
     _note(f"full size {name}: max abs err {ea:.3e}, max rel err {er:.3e}")
     assert torch.isfinite(out.float()).all()
+    _within_visible_v_range(w, t, out)
+    _note(f"full size {name}: every row within the range of its visible V rows")
