@@ -404,9 +404,11 @@ int32_t decode_auto_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_hea
   const int64_t pairs = static_cast<int64_t>(batch) * num_kv_heads * ((group + 15) / 16);
   // Aim for at least ~2048 workgroups (eight per CU) so the tail is short;
   // never split below 256 tokens and never let one workgroup walk more than
-  // kMaxSplit tokens (long contexts then spread over many CUs).
+  // kMaxSplit tokens (long contexts then spread over many CUs).  At 512
+  // contexts of 4k-32k tokens, pieces of 8192 tokens beat 4096 by ~1.3 %
+  // (fewer workgroup starts, half the partial results) and 16384 gains no more.
   constexpr int64_t kWantWGs = 2048;
-  constexpr int64_t kMaxSplit = 4096;
+  constexpr int64_t kMaxSplit = 8192;
   int64_t n = pairs > 0 ? (kWantWGs + pairs - 1) / pairs : 1;
   if (n < 1) n = 1;
   int64_t split = (static_cast<int64_t>(max_context_len) + n - 1) / n;

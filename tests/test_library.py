@@ -84,11 +84,11 @@ def test_decode_plan(lib):
         pkv.decode_workspace_bytes(4, 6, 4, 64, 100)
     for args in [(256, 16, 8, 128, 1024), (512, 64, 8, 128, 32768), (4, 8, 2, 64, 700)]:
         split = pkv.decode_split_tokens(*args)
-        assert 256 <= split <= 4096 and split % 256 == 0
+        assert 256 <= split <= 8192 and split % 256 == 0
     # whole sequences when there are enough (sequence, kv head) pairs to fill the chip
     assert pkv.decode_split_tokens(256, 16, 8, 128, 1024) == 1024
     # long contexts are cut into bounded pieces; tiny batches into single blocks
-    assert pkv.decode_split_tokens(512, 64, 8, 128, 32768) == 4096
+    assert pkv.decode_split_tokens(512, 64, 8, 128, 32768) == 8192
     assert pkv.decode_split_tokens(4, 8, 2, 64, 700) == 256
 
 
