@@ -338,10 +338,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs
     mw[wave * 16 + n16] = m;
     lw[wave * 16 + n16] = lsum;
   }
+  if (n16 < heads_here) {  // padding heads of the MFMA tile are never read back
 #pragma unroll
-  for (int c = 0; c < S::DB; ++c) {
+    for (int c = 0; c < S::DB; ++c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ow[(wave * 16 + n16) * D + 16 * c + 4 * q4 + i] = o[c][i];
+      for (int i = 0; i < 4; ++i) ow[(wave * 16 + n16) * D + 16 * c + 4 * q4 + i] = o[c][i];
+    }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < heads_here * D; idx += kDecThreads) {
