@@ -271,9 +271,11 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
       if (i % kGap == kGap - 1) dma_one<D>(job, lo, i / kGap);
     }
   }
-  // Keep several K operand reads in flight ahead of the MFMAs (LDS latency is
-  // a few MFMA issue slots).
-  sched_reads_ahead<kPfKB * S::KS, kPfKB * S::KS, 4>();
+  // Keep K operand reads in flight ahead of the MFMAs (LDS latency is a few
+  // MFMA issue slots).  Two ahead here and six for the V reads below were the
+  // fastest of 1-8 and 4-16 measured (deeper read-ahead holds more registers
+  // and crowds the next tile's loads).
+  sched_reads_ahead<kPfKB * S::KS, kPfKB * S::KS, 2>();
   // element 4j + i of s[kb] is key k0 + 32 kb + 8 j + 4 h + i of this lane's row
   if (need_mask) {
 #pragma unroll
@@ -312,7 +314,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
       w.o[cb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[u], w.o[cb]);
     }
   }
-  sched_reads_ahead<kPfU * S::DC, 2 * kPfU * S::DC, 8>();
+  sched_reads_ahead<kPfU * S::DC, 2 * kPfU * S::DC, 6>();
 }
 
 // Start of tile step t: wait for this wave's loads of tile t (younger tiles
