@@ -178,8 +178,10 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
     __shared__ int s_count;
     // The collect pass's first loads go out now, so that the row streams in
     // while the threshold is selected (kSmUnroll 16-byte loads per thread in
-    // flight, 128 KiB per row).
-    constexpr int kSmUnroll = 8;
+    // flight, 64 KiB per row; batches of 3-4 were the fastest measured, 8 was
+    // ~3 % and 12-16 ~20 % slower: the first batch queues ahead of the sample
+    // the threshold waits for).
+    constexpr int kSmUnroll = 4;
     // 1024 samples in 64 evenly spaced runs of 16 consecutive entries: 64
     // cache lines per row (1024 lone entries would fetch 1024 lines)
     const int64_t sidx = static_cast<int64_t>(tid >> 4) * (V >> 6) + (tid & 15);
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
     asm volatile("global_load_dword %0, %1, off" : "=v"(zs) : "v"(z + sidx) : "memory");
     // Every wave's sample load goes out before any wave's batch loads (a
     // bare barrier: it orders the issue and waits for no memory), so the
-    // samples do not queue behind 128 KiB of row data.
+    // samples do not queue behind 64 KiB of row data.
     __builtin_amdgcn_s_barrier();
     const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
     const float4* z4 = reinterpret_cast<const float4*>(z);
@@ -199,11 +201,11 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
     // (indices past the row are clamped to its last entry: the loads stay
     // unconditional, and the collect pass skips those entries)
     float4 first[kSmUnroll];
-    static_assert(kSmUnroll == 8, "the wait below counts kSmUnroll loads");
+    static_assert(kSmUnroll == 4, "the wait below counts kSmUnroll loads");
     if (vec) {
 #pragma unroll
       for (int u = 0; u < kSmUnroll; ++u) first[u] = z4[min(tid + static_cast<int64_t>(u) * kSmThreads, n4 - 1)];
-      asm volatile("s_waitcnt vmcnt(8)" : "+v"(zs) : : "memory");
+      asm volatile("s_waitcnt vmcnt(4)" : "+v"(zs) : : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" : "+v"(zs) : : "memory");
     }
