@@ -9,11 +9,16 @@ tensors already resident in HBM.  Several identical copies of the inputs are
 rotated between steps so that a step does not find the previous step's K/V in
 L2 or the Infinity Cache.
 
-Prints one JSON line: whole-step throughput (algorithmic HBM bytes per second
-for decode, algorithmic FLOP/s for prefill) over K steps between two HIP
-events, a roofline object for the attention call (its average launch duration
-from K back-to-back launches between two HIP events on the launch stream), and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line.  Its headline is the long-context decode (batch 512,
+contexts of 4k-32k tokens, 38.7 GB of K/V per step: the largest workload):
+whole-step throughput (algorithmic HBM bytes per second) over K steps between
+two HIP events, a roofline object for the attention call (its average launch
+duration from K back-to-back launches between two HIP events on the launch
+stream), the p10/p50/p90 of single steps, and the fp64 oracle timed on the
+host's cores.  `sub` holds the same record for the other four workloads
+(batch-256 decode, varlen and prefix-cached prefill in FLOP/s, the batch-4
+edge decode), and `ceilings` what a plain copy and a library GEMM reach on
+the same GPU.  With --workload NAME only that workload is timed.
 """
 from __future__ import annotations
 
@@ -33,7 +38,6 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode HBM GB/s (% peak) + decode tok/s; prefill TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-DEFAULT_WORKLOAD = "decode_b256"
 
 
 # ---- algorithmic work ------------------------------------------------------------------
@@ -187,44 +191,62 @@ def summarize_counters(workload: str, fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
-# ---- CPU baseline: the fp64 oracle on a bounded sample ----------------------------------
-def cpu_baseline(w, budget_s: float):
+# ---- CPU baseline: the fp64 oracle on the host's cores ---------------------------------
+def _oracle_units(sub) -> float:
+    """The metric's unit of work of a subset: decode bytes (store + attention) or flops."""
+    return decode_bytes(sub) + store_bytes(sub) if sub.kind == "decode" else prefill_flops(sub)
+
+
+def cpu_baseline(w, pool, budget_s: float):
+    """The oracle as it stands, run per sequence over a process pool on the host's cores.
+
+    A seeded random order of the workload's sequences is dealt to one task per
+    worker process (one BLAS thread each); a task stops after ``budget_s``
+    seconds of oracle time.  The batch's oracle wall time is the busiest
+    process's oracle time (the processes run side by side); input generation
+    is not timed.
+    """
+    order = np.random.Generator(np.random.PCG64(17)).permutation(w.num_seqs).tolist()
+    done, busiest, total, procs = pool.timed(w, order, budget_s)
+    units = _oracle_units(w.subset(done))
+    if w.kind == "decode":
+        value, unit, scale = units / busiest / 1e9, "GB/s", 1e9
+    else:
+        value, unit, scale = units / busiest / 1e12, "TFLOP/s", 1e12
+    return {"value": value, "unit": unit, "cores": procs, "kind": "oracle",
+            "per_core_value": units / total / scale,
+            "sample": f"{len(done)} of {w.num_seqs} sequences (store + attention, fp64 NumPy), "
+                      f"{procs} worker processes with one thread each, {total:.1f} s of oracle "
+                      f"time in all, {busiest:.2f} s in the busiest process; input generation "
+                      f"untimed"}
+
+
+def cpu_baseline_one_core(w, budget_s: float):
+    """The same oracle on one thread of this process (the small edge workload)."""
     import oracle
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limiter = None
-    rng = np.random.Generator(np.random.PCG64(17))
-    order = rng.permutation(w.num_seqs)
-    done, t_work, units = [], 0.0, 0
-    for s in order:
-        sub = w.subset([int(s)])
-        h = sub.host_inputs()  # input generation is not timed
+    done, t_work = [], 0.0
+    for s in range(w.num_seqs):
+        sub = w.subset([s])
+        h = sub.host_inputs()
         t0 = time.perf_counter()
         kc, vc = oracle.store_kvcache(h["k_cache"], h["v_cache"], h["k_new"], h["v_new"],
                                       h["slot_mapping"])
-        if w.kind == "decode":
-            oracle.paged_decode(h["q"], kc, vc, h["block_tables"], h["context_lens"],
-                                sub.block_size, sub.scale)
-            units += decode_bytes(sub) + store_bytes(sub)
-        else:
-            oracle.paged_prefill(h["q"], kc, vc, h["cu_seqlens_q"], h["cu_seqlens_k"],
-                                 h["block_tables"], sub.block_size, sub.scale, sub.causal)
-            units += prefill_flops(sub)
+        oracle.paged_decode(h["q"], kc, vc, h["block_tables"], h["context_lens"], sub.block_size,
+                            sub.scale)
         t_work += time.perf_counter() - t0
-        done.append(int(s))
+        done.append(s)
         if t_work >= budget_s:
             break
     if limiter is not None:
         limiter.unregister()
-    if w.kind == "decode":
-        value, unit = units / t_work / 1e9, "GB/s"
-    else:
-        value, unit = units / t_work / 1e12, "TFLOP/s"
-    return {"value": value, "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} of {w.num_seqs} sequences (store + attention, fp64 NumPy, "
-                      f"one thread), {t_work:.1f} s of oracle time; input generation untimed"}
+    units = _oracle_units(w.subset(done))
+    return {"value": units / t_work / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {w.num_seqs} sequences, one thread, {t_work:.3f} s"}
 
 
 # ---- sampling (the adjacent next-token step) ----------------------------------------------
@@ -295,50 +317,67 @@ def run_sampling(args, torch, pkv, dev):
 
 
 # ---- GPU run ----------------------------------------------------------------------------
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--replicas", type=int, default=0, help="input copies rotated (0 = auto)")
-    ap.add_argument("--split-tokens", type=int, default=0, help="decode split (0 = library's choice)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="decode: also time the step replayed from a captured HIP graph")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="end with a 1 GiB device copy (counter calibration under rocprofv3)")
-    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 --pmc runs into profiles/traffic_<workload>.json")
-    args = ap.parse_args()
+def unique_step_bytes(w) -> int:
+    """Bytes one step touches, each distinct byte once: Q, O, the K/V of every distinct
+    key position (a shared prefix once, not once per sequence) and the store's rows.
+    Sizes the number of input copies rotated between steps."""
+    kv_tokens = w.prefix_len + int((w.hist + w.lq).sum())
+    kv = kv_tokens * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = 2 * w.num_q_rows * w.num_q_heads * w.head_dim * 2
+    return kv + qo + store_bytes(w)
 
-    if args.counters:
-        print(json.dumps(summarize_counters(args.workload, *args.counters)), flush=True)
-        return
 
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the data plane has no cross-GPU step in this build)", file=sys.stderr)
-        sys.exit(2)
+def _pct(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
 
-    import torch
-    import paged_kv_cache_419_amd as pkv
+
+def measure_ceilings(torch, dev, reps: int = 10) -> dict:
+    """What plain library kernels reach on this machine, beside the published peaks: a
+    2 GiB device-to-device copy (bytes read + written per second) and a bf16 GEMM of
+    8192^3 through torch (hipBLASLt), each the median of `reps` timed calls."""
+    out = {}
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+
+    def med_ms(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    ms = med_ms(lambda: dst.copy_(src))
+    out["copy_gbs"] = 2 * n / (ms * 1e-3) / 1e9
+    out["copy_frac_of_hbm_peak"] = out["copy_gbs"] / HBM_PEAK_GBS
+    ms = med_ms(lambda: torch.mm(a, b, out=c))
+    out["gemm_bf16_tflops"] = 2 * 8192 ** 3 / (ms * 1e-3) / 1e12
+    out["gemm_frac_of_mfma_peak"] = out["gemm_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    out["how"] = ("median of 10 event-timed calls: torch copy_ of 2 GiB (read + write bytes), "
+                  "torch.mm bf16 8192x8192x8192 (hipBLASLt)")
+    del src, dst, a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure(name, args, torch, pkv, dev, pool, cpu_budget):
+    """Time one workload: K whole steps (store + attention) back to back, each call's
+    own average launch duration, the spread of single steps, an oracle check of what
+    was timed, and the oracle on the host's cores."""
     import workload as W
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    pkv.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.workload == SAMPLE_WORKLOAD:
-        run_sampling(args, torch, pkv, dev)
-        return
-    w = W.make(args.workload)
+    w = W.make(name)
     decode = w.kind == "decode"
-    work_set = (decode_bytes(w) if decode else prefill_bytes(w)) + store_bytes(w)
-    reps = args.replicas or max(1, min(4, math.ceil(2.0e9 / work_set)))
+    reps = args.replicas or max(1, min(4, math.ceil(2.0e9 / unique_step_bytes(w))))
     copies = [w.materialize(dev) for _ in range(reps)]
     outs = [torch.empty_like(c["q"]) for c in copies]
     split = args.split_tokens
@@ -363,11 +402,13 @@ def main():
                                          c["cu_seqlens_k"], c["block_tables"], max_q, max_k,
                                          w.block_size, w.scale, w.causal, workspace)
 
-    for i in range(args.warmup):
+    def step(i):
         store(copies[i % reps])
         attend(copies[i % reps], outs[i % reps])
-    torch.cuda.synchronize()
 
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def timed(body) -> float:
@@ -382,45 +423,57 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    def step(i):
-        store(copies[i % reps])
-        attend(copies[i % reps], outs[i % reps])
+    def spread(body):
+        """Per-iteration ms from an event between consecutive iterations (a separate pass)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(args.steps):
+            body(i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
 
-    # the timed region: K whole steps (store + attention); then each call's own
-    # launch duration, from K back-to-back launches of that call alone
+    # the timed region: K whole steps (store + attention); then the attention call's
+    # own launch duration from K back-to-back launches of that call alone
     ms_step = timed(step)
     attn_ms = timed(lambda i: attend(copies[i % reps], outs[i % reps]))
-    store_ms = timed(lambda i: store(copies[i % reps]))
+    steps_ms = spread(step)
+    attn_each = spread(lambda i: attend(copies[i % reps], outs[i % reps]))
 
     if decode:
-        step_bytes = decode_bytes(w) + store_bytes(w)
-        value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
+        step_units = decode_bytes(w) + store_bytes(w)
+        value, unit = step_units / (ms_step * 1e-3) / 1e9, "GB/s"
         achieved = decode_bytes(w) / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
         kernel = "paged_decode_attention"
+        roof["algorithmic_bytes"] = decode_bytes(w)
     else:
         value, unit = prefill_flops(w) / (ms_step * 1e-3) / 1e12, "TFLOP/s"
         achieved = prefill_flops(w) / (attn_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
         kernel = "varlen_prefill_attention"
-    roof["traffic"] = measured_traffic(args.workload, kernel)
+        roof["algorithmic_flops"] = prefill_flops(w)
+    roof["traffic"] = measured_traffic(name, kernel)
     roof["kernel"] = kernel
     roof["kernel_ms"] = attn_ms
 
-    # correctness of what was timed: one sampled sequence against the oracle
+    # correctness of what was timed: the longest sequence against the oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import gpu_harness as H
     probe = [int(np.argmax(w.lk if decode else w.lq))]
     H.check_against_oracle(w, outs[0], probe)
 
     rec = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "value": value, "unit": unit, "ms_per_step": ms_step,
+        "step_ms_p10": _pct(steps_ms, 10), "step_ms_p50": _pct(steps_ms, 50),
+        "step_ms_p90": _pct(steps_ms, 90),
+        "attention_ms": attn_ms, "attention_ms_p10": _pct(attn_each, 10),
+        "attention_ms_p90": _pct(attn_each, 90),
         "config": {
-            "workload": args.workload, "kind": w.kind, "sequences": w.num_seqs,
+            "workload": name, "kind": w.kind, "sequences": w.num_seqs,
             "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
             "context_tokens": int(w.lk.sum()), "new_tokens": w.num_new_tokens,
@@ -428,29 +481,22 @@ def main():
                                                               w.num_kv_heads, w.head_dim,
                                                               w.max_context_len)) if decode else None,
             "input_copies_rotated": reps, "parallelism": "none (1 GPU)"},
-        "store_ms": store_ms, "attention_ms": attn_ms,
         "roofline": roof,
     }
     if decode:
         rec["decode_tok_per_s"] = w.num_seqs / (ms_step * 1e-3)
+        rec["hbm_frac"] = value / HBM_PEAK_GBS
         if int(w.lq.min()) == 1 and w.pad_tokens == 0 and not args.copy_probe:
             # the same step as one fused kernel (store the new tokens and attend)
-            def fused(c, out):
+            def fused(i):
+                c, out = copies[i % reps], outs[i % reps]
                 pkv.store_and_decode(out, c["q"], c["k_new"], c["v_new"], c["k_cache"], c["v_cache"],
                                      c["slot_mapping"], c["block_tables"], c["context_lens"],
                                      w.block_size, w.max_context_len, w.scale, split, workspace)
             for i in range(args.warmup):
-                fused(copies[i % reps], outs[i % reps])
-            torch.cuda.synchronize()
-            f0 = torch.cuda.Event(enable_timing=True)
-            f1 = torch.cuda.Event(enable_timing=True)
-            f0.record(stream)
-            for i in range(args.steps):
-                fused(copies[i % reps], outs[i % reps])
-            f1.record(stream)
-            torch.cuda.synchronize()
+                fused(i)
+            rec["fused_ms_per_step"] = timed(fused)
             H.check_against_oracle(w, outs[0], probe)
-            rec["fused_ms_per_step"] = f0.elapsed_time(f1) / args.steps
             rec["fused_decode_tok_per_s"] = w.num_seqs / (rec["fused_ms_per_step"] * 1e-3)
         if args.graph:
             # the same step (store + decode) captured once per input copy and replayed
@@ -463,22 +509,96 @@ def main():
                 graphs.append(g)
             for i in range(args.warmup):
                 graphs[i % reps].replay()
-            torch.cuda.synchronize()
-            g0 = torch.cuda.Event(enable_timing=True)
-            g1 = torch.cuda.Event(enable_timing=True)
-            g0.record(stream)
-            for i in range(args.steps):
-                graphs[i % reps].replay()
-            g1.record(stream)
-            torch.cuda.synchronize()
-            rec["graph_ms_per_step"] = g0.elapsed_time(g1) / args.steps
+            rec["graph_ms_per_step"] = timed(lambda i: graphs[i % reps].replay())
             rec["graph_decode_tok_per_s"] = w.num_seqs / (rec["graph_ms_per_step"] * 1e-3)
-        rec["hbm_frac"] = value / HBM_PEAK_GBS
     else:
-        rec["mfma_frac"] = value / MFMA_BF16_PEAK_TFLOPS
+        # the store of this step's tokens (36k tokens here: long enough to time on its own)
+        store_ms = timed(lambda i: store(copies[i % reps]))
+        rec["store_ms"] = store_ms
         rec["store_gbs"] = store_bytes(w) / (store_ms * 1e-3) / 1e9
+        rec["mfma_frac"] = value / MFMA_BF16_PEAK_TFLOPS
+    del copies, outs, workspace
+    torch.cuda.empty_cache()
+    if pool is not None:
+        rec["cpu_baseline"] = cpu_baseline(w, pool, cpu_budget)
+        if name == "decode_edge_b4":
+            rec["cpu_baseline_one_core"] = cpu_baseline_one_core(w, cpu_budget)
+    return rec
+
+
+HEADLINE = "decode_long_b512"  # the largest single-GPU workload (38.7 GB of K/V per step)
+SUB_WORKLOADS = ("decode_b256", "prefill_varlen_s64", "prefill_prefix_s128", "decode_edge_b4")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help=f"time this workload alone (default: {HEADLINE} as the headline, with "
+                         "the other data-plane workloads as sub-records)")
+    ap.add_argument("--replicas", type=int, default=0, help="input copies rotated (0 = auto)")
+    ap.add_argument("--split-tokens", type=int, default=0, help="decode split (0 = library's choice)")
+    ap.add_argument("--cpu-budget", type=float, default=1.5,
+                    help="seconds of oracle time per host worker process (headline workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: also time the step replayed from a captured HIP graph")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="end with a 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/traffic_<workload>.json")
+    args = ap.parse_args()
+
+    if args.counters:
+        print(json.dumps(summarize_counters(args.workload, *args.counters)), flush=True)
+        return
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the data plane has no cross-GPU step in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_419_amd as pkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pkv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload == SAMPLE_WORKLOAD:
+        run_sampling(args, torch, pkv, dev)
+        return
+    single = args.workload is not None
+    headline = args.workload or HEADLINE
+    pool = None
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        from oracle.pool import OraclePool
+        pool = OraclePool()
+    try:
+        head = measure(headline, args, torch, pkv, dev, pool, args.cpu_budget)
+        subs = {}
+        if not single:
+            for name in SUB_WORKLOADS:
+                subs[name] = measure(name, args, torch, pkv, dev, pool, args.cpu_budget / 2)
+    finally:
+        if pool is not None:
+            pool.close()
+    rec = {
+        "metric": METRIC, "value": head.pop("value"), "unit": head.pop("unit"), "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+    }
+    rec.update(head)
+    if subs:
+        rec["sub"] = subs
+    if not args.no_ceilings and not args.copy_probe:
+        rec["ceilings"] = measure_ceilings(torch, dev)
     if args.copy_probe:
         copy_probe(torch, dev)
     print(json.dumps(rec), flush=True)

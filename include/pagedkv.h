@@ -1,7 +1,8 @@
 /*
  * pagedkv.h -- C ABI of the paged KV-cache data plane for MI355X (gfx950).
  *
- * Three operations, as the Nano-vLLM write-ups describe the data plane:
+ * Five operations of the data plane the Nano-vLLM write-ups describe, plus
+ * the host-side block manager that feeds them (declared further down):
  *
  *   pkv_store_kvcache             write each new token's K and V rows into the
  *                                 block-paged cache at its slot-mapping entry
@@ -72,8 +73,9 @@ typedef enum pkv_status {
  *   k_cache[slot_mapping[i]] = k[i]  and  v_cache[slot_mapping[i]] = v[i]
  * (hotdry.top, PagedAttention section: new keys and values written at their
  * slot-mapping offsets; "Nano-vLLM part 1", section 5.2: decode passes the
- * slot mapping).  A negative slot is a padding entry and is skipped.  Rows of
- * the cache not named by the mapping keep their contents bit for bit.
+ * slot mapping).  A negative slot is a padding entry and is skipped; a slot
+ * >= num_slots is skipped too (as in pkv_store_and_decode).  Rows of the
+ * cache not named by the mapping keep their contents bit for bit.
  *
  *   k, v          device bf16 [num_tokens, num_kv_heads, head_dim]
  *   k_cache,

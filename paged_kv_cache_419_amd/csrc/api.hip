@@ -100,7 +100,7 @@ pkv_status pkv_store_kvcache(const void* k, const void* v, void* k_cache, void* 
   if (num_tokens > (int64_t{1} << 31) - 1 || row > (int64_t{1} << 20))
     return fail(PKV_ERR_UNSUPPORTED, "num_tokens or row size too large");
   return hip_status(pkv::launch_store_kvcache(k, v, k_cache, v_cache, slot_mapping, num_tokens,
-                                              static_cast<int32_t>(row),
+                                              num_slots, static_cast<int32_t>(row),
                                               static_cast<hipStream_t>(stream)),
                     "store_kvcache launch");
 }

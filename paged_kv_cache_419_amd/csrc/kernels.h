@@ -9,7 +9,7 @@ namespace pkv {
 
 hipError_t launch_store_kvcache(const void* k, const void* v, void* k_cache, void* v_cache,
                                 const int32_t* slot_mapping, int64_t num_tokens,
-                                int32_t row_elems, hipStream_t stream);
+                                int64_t num_slots, int32_t row_elems, hipStream_t stream);
 
 struct DecodeArgs {
   void* out;

@@ -23,8 +23,9 @@
 // next tile's loads are in flight while the current tile is computed.  Rows
 // are stored with XOR-swizzled 16-byte chunks so that both the K operand reads
 // and the transposing V reads are free of bank conflicts.  Key rows past Lk
-// are redirected to key Lk - 1 (a live row), so stale or poisoned slots are
-// never read; their scores are masked.
+// fall outside the wave's buffer descriptor, whose range ends after the last
+// live row: they fetch nothing and arrive as zeros, so stale or poisoned slots
+// are never read; their scores are masked.
 //
 // Matrix cores.  Each wave computes S^T[key][row] = K Q^T on 32x32x16 bf16
 // MFMAs with Q^T held in registers.  In that output layout a lane holds 32

@@ -114,6 +114,11 @@ class DecodeGraphs:
         batch = q.shape[0]
         if block_tables.shape[1] > self.max_blocks_per_seq:
             raise ValueError("block table wider than the captured one")
+        if context_lens.device.type == "cpu" and batch and int(context_lens.max()) > self.max_context_len:
+            # the captured launch covers max_context_len positions: a longer context
+            # would be cut short (and the fused step would not store its new token)
+            raise ValueError(f"context length {int(context_lens.max())} exceeds the captured "
+                             f"bound {self.max_context_len}")
         bk = self._b[self.bucket_for(batch)]
         bk.q[:batch].copy_(q)
         bk.k[:batch].copy_(k)

@@ -28,6 +28,42 @@ def _f64(bits):
     return oracle.bf16_to_f64(bits)
 
 
+# ---- number format: bf16 bit patterns widened to fp64 ------------------------------
+def _bf16_from_fields(bits: int) -> float:
+    """bf16 value from its fields (1 sign, 8 exponent bits biased by 127, 7 fraction
+    bits; exponent 0 is zero or subnormal, 255 is inf or NaN), in Python integers and
+    math.ldexp: a decoding of the format's definition that shares nothing with the
+    oracle's shift-and-reinterpret route."""
+    sign = -1.0 if bits >> 15 else 1.0
+    exp = (bits >> 7) & 0xFF
+    frac = bits & 0x7F
+    if exp == 0xFF:
+        return sign * math.inf if frac == 0 else math.nan
+    if exp == 0:
+        return sign * math.ldexp(frac, -126 - 7)
+    return sign * math.ldexp(128 + frac, exp - 127 - 7)
+
+
+def pin_bf16_widening():
+    """All 65,536 bf16 bit patterns: the oracle's widening equals torch's bfloat16 ->
+    float64 conversion and the field-by-field decoding, with the sign of zero kept
+    and NaN exactly where the format puts it."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.bf16_to_f64(bits)
+    assert got.dtype == np.float64 and got.shape == bits.shape
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    fields = np.array([_bf16_from_fields(int(b)) for b in bits], dtype=np.float64)
+    for ref in (lib, fields):
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), "NaN patterns differ"
+        assert np.array_equal(got[~nan], ref[~nan]), "values differ"
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), "signs differ"
+    # a few patterns spelled out: 1, -2, the smallest subnormal, the largest finite, inf
+    for b, v in ((0x3F80, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -133),
+                 (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127), (0xFF80, -math.inf)):
+        assert oracle.bf16_to_f64(np.array([b], np.uint16))[0] == v, hex(b)
+
+
 # ---- the pages' own worked example --------------------------------------------------
 def pin_pages_block_example():
     """700 tokens in 256-token blocks: 3 blocks, 188 in the last, 68 idle."""

@@ -88,6 +88,11 @@ def test_graph_bucket_choice_and_padding():
     slots = np.sort(w.slot_mapping[w.slot_mapping >= 0])
     assert np.array_equal(np.nonzero(changed.cpu().numpy())[0], slots)
     H.check_against_oracle(w, out, list(range(w.num_seqs)))
+    # a context longer than the captured bound is refused before anything runs
+    too_long = torch.from_numpy(w.context_lens.copy())
+    too_long[0] = w.max_context_len + 1
+    with pytest.raises(ValueError):
+        graphs.run(t["q"], t["k_new"], t["v_new"], t["slot_mapping"], t["block_tables"], too_long)
 
 
 def test_fused_graph_replays_match_eager_fused_call():

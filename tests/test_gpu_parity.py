@@ -63,6 +63,24 @@ def test_attention_small(name):
     assert ok, f"max abs {ea:.3e} rel {er:.3e}"
 
 
+def test_store_skips_slots_past_the_cache():
+    """Slots >= num_slots are skipped like padding entries: the image equals the
+    oracle's store of the same batch with those entries marked as padding."""
+    w = cases.get("decode_mha_bs32")
+    h = cases.inputs("decode_mha_bs32")
+    t = w.materialize("cuda")
+    sm = t["slot_mapping"].clone()
+    sm[0] = w.num_slots          # one past the end
+    sm[1] = w.num_slots + 4096   # far past it
+    pkv.store_kvcache(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], sm)
+    torch.cuda.synchronize()
+    sm_ref = sm.cpu().numpy().copy()
+    sm_ref[sm_ref >= w.num_slots] = -1
+    kc, vc = oracle.store_kvcache(h["k_cache"], h["v_cache"], h["k_new"], h["v_new"], sm_ref)
+    assert (bf16_bits(t["k_cache"]) == kc).all()
+    assert (bf16_bits(t["v_cache"]) == vc).all()
+
+
 @pytest.mark.parametrize("split", [32, 64, 128, 256, 2048])
 @pytest.mark.parametrize("name", ["decode_edge_b4", "decode_tiny_bs16", "decode_g16",
                                   "decode_long_b512[2]"])
@@ -138,18 +156,34 @@ def _within_visible_v_range(w, t, out):
         assert not bool(bad.any()), f"sequence {s}: {int(bad.sum())} outputs outside the range of the V rows they see"
 
 
-def _samples(w, k):
+def _stratified(w, k):
+    """At least k sequences spread over the length range: the shortest, the longest and
+    one seeded pick from each of k equal-count bins of the sequences sorted by length."""
     lens = w.lk if w.kind == "decode" else w.lq
+    order = np.argsort(lens, kind="stable")
     rng = np.random.Generator(np.random.PCG64(11))
-    pick = {int(np.argmin(lens)), int(np.argmax(lens))}
-    pick.update(int(x) for x in rng.choice(w.num_seqs, size=min(k, w.num_seqs), replace=False))
+    pick = {int(order[0]), int(order[-1])}
+    for b in np.array_split(order, k):
+        if b.size:
+            pick.add(int(rng.choice(b)))
     return sorted(pick)
 
 
-@pytest.mark.parametrize("name,k", [("decode_edge_b4", 4), ("decode_b256", 24),
-                                    ("prefill_varlen_s64", 3), ("prefill_prefix_s128", 3),
-                                    ("decode_long_b512", 4)])
-def test_full_size(name, k):
+@pytest.fixture(scope="module")
+def oracle_pool():
+    from oracle.pool import OraclePool
+    with OraclePool() as pool:
+        yield pool
+
+
+# every sequence of the first four workloads; a 32-bin stratified sample of the
+# 512 long contexts (the oracle regenerates each one's 4k-32k positions on the host)
+FULL = [("decode_edge_b4", None), ("decode_b256", None), ("prefill_varlen_s64", None),
+        ("prefill_prefix_s128", None), ("decode_long_b512", 32)]
+
+
+@pytest.mark.parametrize("name,strata", FULL)
+def test_full_size(name, strata, oracle_pool):
     w = W.make(name)
     _note(f"full size {name}: materialize")
     t = w.materialize("cuda")
@@ -168,10 +202,16 @@ def test_full_size(name, k):
     assert torch.equal(t["v_cache"][live].view(torch.int16), t["v_new"][slots >= 0].view(torch.int16))
     assert torch.equal(t["k_cache"][probe].view(torch.int16), before_k.view(torch.int16))
     assert torch.equal(t["v_cache"][probe].view(torch.int16), before_v.view(torch.int16))
-    seqs = _samples(w, k) if w.num_seqs > 4 else list(range(w.num_seqs))
-    _note(f"full size {name}: oracle on {len(seqs)} sequences")
-    ea, er = H.check_against_oracle(w, out, seqs)
-    _note(f"full size {name}: max abs err {ea:.3e}, max rel err {er:.3e}")
+    seqs = list(range(w.num_seqs)) if strata is None else _stratified(w, strata)
+    bits = bf16_bits(out)
+    rows = [bits[H.rows_for(w, [s])] for s in seqs]
+    _note(f"full size {name}: oracle on {len(seqs)} of {w.num_seqs} sequences, "
+          f"{oracle_pool.workers} host processes")
+    n_rows, n_bad, ea, er, first_bad = oracle_pool.compare(w, seqs, rows)
+    _note(f"full size {name}: {n_rows} rows, max abs err {ea:.3e}, max rel err {er:.3e}")
+    assert n_rows == sum(r.shape[0] for r in rows)
+    assert n_bad == 0, (f"{name}: {n_bad} elements outside 1e-2 + 1e-2 |ref| (first in sequence "
+                        f"{first_bad}); max abs err {ea:.3e}")
     assert torch.isfinite(out.float()).all()
     _within_visible_v_range(w, t, out)
     _note(f"full size {name}: every row within the range of its visible V rows")

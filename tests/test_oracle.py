@@ -11,6 +11,10 @@ TINY = ["decode_edge_b4", "decode_tiny_bs16", "decode_mha_bs32", "prefill_ragged
         "prefill_hist_bs32", "prefill_prefix_bs16"]
 
 
+def test_bf16_widening():
+    P.pin_bf16_widening()
+
+
 def test_pages_block_example():
     P.pin_pages_block_example()
 

@@ -92,3 +92,34 @@ def test_mutant_store_writes_padding(monkeypatch):
     import oracle
     monkeypatch.setattr(oracle, "store_kvcache", bad_store)
     assert _any_caught([(P.pin_store, "decode_mha_bs32")])
+
+
+def _patch_widening(monkeypatch, fn):
+    import oracle
+    monkeypatch.setattr(OA, "bf16_to_f64", fn)
+    monkeypatch.setattr(oracle, "bf16_to_f64", fn)
+
+
+def test_mutant_widening_shift(monkeypatch):
+    # bf16 bits placed one position too low in the fp32 word
+    def bad(bits):
+        b = np.ascontiguousarray(bits, dtype=np.uint16)
+        return (b.astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+    _patch_widening(monkeypatch, bad)
+    assert _any_caught([(P.pin_bf16_widening,)])
+
+
+def test_mutant_widening_sign_dropped(monkeypatch):
+    def bad(bits):
+        b = np.ascontiguousarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    _patch_widening(monkeypatch, bad)
+    assert _any_caught([(P.pin_bf16_widening,)])
+
+
+def test_mutant_widening_as_fp16(monkeypatch):
+    # the bits read as IEEE half precision instead of bfloat16
+    def bad(bits):
+        return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    _patch_widening(monkeypatch, bad)
+    assert _any_caught([(P.pin_bf16_widening,)])
