@@ -36,11 +36,20 @@ def host_cores() -> int:
 
 
 def _init_worker():
+    # one thread per worker for every library: BLAS, OpenMP and torch's own pool
+    # (the input generator runs torch CPU ops), so the pool uses one core per process
+    import torch
+    torch.set_num_threads(1)
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(limits=1)
     except Exception:  # pragma: no cover - threadpoolctl is installed here
         pass
+
+
+def _ready():
+    import torch
+    return os.getpid(), torch.get_num_threads()
 
 
 def _sequence_ref(w, s: int) -> np.ndarray:
@@ -111,11 +120,20 @@ def _timed_task(w, seqs: Sequence[int], budget_s: float):
 class OraclePool:
     """A pool of spawned worker processes running the oracle per sequence."""
 
-    def __init__(self, workers: Optional[int] = None):
+    def __init__(self, workers: Optional[int] = None, log=None, timeout_s: float = 900.0):
         self.workers = workers or host_cores()
+        self.log = log or (lambda msg: None)
+        self.timeout_s = timeout_s
         self._ex = cf.ProcessPoolExecutor(max_workers=self.workers,
                                           mp_context=mp.get_context("spawn"),
                                           initializer=_init_worker)
+        # start every worker now (the executor would otherwise start them one per
+        # submitted task) and check that each came up with one thread
+        t0 = time.perf_counter()
+        futs = [self._ex.submit(_ready) for _ in range(self.workers)]
+        ready = [f.result(timeout=self.timeout_s) for f in futs]
+        self.log(f"oracle pool: {self.workers} workers up in {time.perf_counter() - t0:.1f} s, "
+                 f"threads per worker {sorted({t for _, t in ready})}")
 
     def close(self):
         self._ex.shutdown(wait=True, cancel_futures=True)
@@ -140,8 +158,12 @@ class OraclePool:
         rows = bad = 0
         ea = er = 0.0
         first_bad = -1
-        for f in futs:
+        t0 = time.perf_counter()
+        for k, f in enumerate(cf.as_completed(futs, timeout=self.timeout_s)):
             r, b, a, e, fb = f.result()
+            if (k + 1) % max(1, len(futs) // 4) == 0 or k + 1 == len(futs):
+                self.log(f"oracle pool: {k + 1} of {len(futs)} chunks compared "
+                         f"({time.perf_counter() - t0:.1f} s)")
             rows += r
             bad += b
             ea, er = max(ea, a), max(er, e)
@@ -162,7 +184,7 @@ class OraclePool:
         shares = [list(seqs[k::self.workers]) for k in range(self.workers)]
         futs = [self._ex.submit(_timed_task, w, sh, budget_s) for sh in shares if sh]
         per_pid, done, total = {}, [], 0.0
-        for f in futs:
+        for f in cf.as_completed(futs, timeout=self.timeout_s):
             pid, t, d = f.result()
             per_pid[pid] = per_pid.get(pid, 0.0) + t
             total += t

@@ -52,6 +52,40 @@ class PagedKVError(RuntimeError):
 _lib = None
 
 
+def _declare_block_manager(lib: ctypes.CDLL) -> None:
+    """Argument and result types of the block manager's entry points (pkv_bm_*)."""
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.pkv_bm_create.argtypes = [i32, i32]
+    lib.pkv_bm_create.restype = vp
+    lib.pkv_bm_destroy.argtypes = [vp]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_num_free.argtypes = [vp]
+    lib.pkv_bm_num_free.restype = i32
+    lib.pkv_bm_allocate.argtypes = [vp, i64, i32p, i32]
+    lib.pkv_bm_allocate.restype = i32
+    lib.pkv_bm_append.argtypes = [vp, i64, i32]
+    lib.pkv_bm_append.restype = i32
+    lib.pkv_bm_free.argtypes = [vp, i64]
+    lib.pkv_bm_free.restype = i32
+    lib.pkv_bm_seq_len.argtypes = [vp, i64]
+    lib.pkv_bm_seq_len.restype = i32
+    lib.pkv_bm_block_table.argtypes = [vp, i64, i32p, i32]
+    lib.pkv_bm_block_table.restype = i32
+    lib.pkv_bm_slots.argtypes = [vp, i64, i32, i32, i32p]
+    lib.pkv_bm_slots.restype = i32
+    lib.pkv_bm_ref_count.argtypes = [vp, i32]
+    lib.pkv_bm_ref_count.restype = i32
+
+
+def load_block_manager(path: str) -> ctypes.CDLL:
+    """A host-only build of the block manager (its pkv_bm_* entry points alone),
+    such as the sanitizer build the CPU tests make; the data-plane calls are not in it."""
+    lib = ctypes.CDLL(path)
+    _declare_block_manager(lib)
+    return lib
+
+
 def load(path: Optional[str] = None) -> ctypes.CDLL:
     """Load the library once (raises if it has not been built)."""
     global _lib
@@ -81,27 +115,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pkv_varlen_prefill_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                                  i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.pkv_varlen_prefill_attention.restype = ctypes.c_int
-    i32p = ctypes.POINTER(ctypes.c_int32)
-    lib.pkv_bm_create.argtypes = [i32, i32]
-    lib.pkv_bm_create.restype = vp
-    lib.pkv_bm_destroy.argtypes = [vp]
-    lib.pkv_bm_destroy.restype = None
-    lib.pkv_bm_num_free.argtypes = [vp]
-    lib.pkv_bm_num_free.restype = i32
-    lib.pkv_bm_allocate.argtypes = [vp, i64, i32p, i32]
-    lib.pkv_bm_allocate.restype = i32
-    lib.pkv_bm_append.argtypes = [vp, i64, i32]
-    lib.pkv_bm_append.restype = i32
-    lib.pkv_bm_free.argtypes = [vp, i64]
-    lib.pkv_bm_free.restype = i32
-    lib.pkv_bm_seq_len.argtypes = [vp, i64]
-    lib.pkv_bm_seq_len.restype = i32
-    lib.pkv_bm_block_table.argtypes = [vp, i64, i32p, i32]
-    lib.pkv_bm_block_table.restype = i32
-    lib.pkv_bm_slots.argtypes = [vp, i64, i32, i32, i32p]
-    lib.pkv_bm_slots.restype = i32
-    lib.pkv_bm_ref_count.argtypes = [vp, i32]
-    lib.pkv_bm_ref_count.restype = i32
+    _declare_block_manager(lib)
     lib.pkv_last_error.argtypes = []
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.argtypes = []

@@ -9,6 +9,7 @@ and "no space" answers on which the caller preempts a sequence.
 from __future__ import annotations
 
 import ctypes
+import os
 from typing import List, Sequence
 
 import numpy as np
@@ -28,9 +29,16 @@ class NoSpace(RuntimeError):
     """Not enough free blocks; the manager is unchanged (preempt a sequence)."""
 
 
+def _library() -> ctypes.CDLL:
+    # PKV_BM_LIBRARY names a host-only build of the same C++ source (the CPU tests
+    # load one built with AddressSanitizer and UndefinedBehaviorSanitizer)
+    path = os.environ.get("PKV_BM_LIBRARY")
+    return binding.load_block_manager(path) if path else binding.load()
+
+
 class BlockManager:
     def __init__(self, num_blocks: int, block_size: int = 256):
-        self._lib = binding.load()
+        self._lib = _library()
         self._h = self._lib.pkv_bm_create(num_blocks, block_size)
         if not self._h:
             raise ValueError(f"bad sizes: {num_blocks} blocks of {block_size} tokens")

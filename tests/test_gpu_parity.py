@@ -172,7 +172,7 @@ def _stratified(w, k):
 @pytest.fixture(scope="module")
 def oracle_pool():
     from oracle.pool import OraclePool
-    with OraclePool() as pool:
+    with OraclePool(log=_note, timeout_s=600.0) as pool:
         yield pool
 
 
