@@ -220,6 +220,36 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
                                         float scale, int32_t causal, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* Bytes of the fixed per-GPU scratch of pkv_varlen_prefill_attention_noalloc. */
+#define PKV_PREFILL_NOALLOC_SCRATCH_BYTES ((size_t)2 << 20)
+
+/*
+ * pkv_varlen_prefill_attention without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It computes exactly what
+ * pkv_varlen_prefill_attention computes (same checks, same kernels, the same
+ * output bit for bit) and allocates nothing: its work list lives in a fixed
+ * device array of PKV_PREFILL_NOALLOC_SCRATCH_BYTES bytes (2 MiB),
+ * which each GPU the library runs on holds from the first call there until
+ * the process ends.  Batches whose pkv_prefill_workspace_bytes(...) exceeds
+ * that size are refused with PKV_ERR_UNSUPPORTED before anything is enqueued
+ * (about 32,000 (sequence, 128-row query tile) pairs at 4 query heads per kv
+ * head).  Every call on one GPU uses that GPU's one array: calls that may
+ * overlap in time on one GPU (different streams, different host threads) race
+ * and must not be issued; each call rewrites the array from the start, so
+ * stale contents from an earlier call do not matter.  Arguments as for
+ * pkv_varlen_prefill_attention.
+ */
+pkv_status pkv_varlen_prefill_attention_noalloc(void* out, const void* q, const void* k_cache,
+                                                const void* v_cache, const int32_t* cu_seqlens_q,
+                                                const int32_t* cu_seqlens_k,
+                                                const int32_t* block_tables, int32_t num_seqs,
+                                                int64_t total_q, int32_t max_seqlen_q,
+                                                int32_t max_seqlen_k, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t max_blocks_per_seq,
+                                                float scale, int32_t causal, void* stream);
+
 /*
  * Next-token sampling with temperature and top-k ("Nano-vLLM part 1",
  * section 5.4: the logits over the vocabulary become one token by sampling,

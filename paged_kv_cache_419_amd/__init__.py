@@ -8,5 +8,6 @@ tensors into the C calls.
 from .binding import (  # noqa: F401
     EXPORTS, LIB_PATH, PagedKVError, decode_split_tokens, decode_workspace_bytes, load,
     paged_decode_attention, prefill_workspace_bytes, store_and_decode, store_kvcache,
-    topk_sample, varlen_prefill_attention, version,
+    topk_sample, varlen_prefill_attention, varlen_prefill_attention_noalloc,
+    PREFILL_NOALLOC_SCRATCH_BYTES, version,
 )

@@ -28,6 +28,7 @@ EXPORTS = (
     "pkv_topk_sample",
     "pkv_prefill_workspace_bytes",
     "pkv_varlen_prefill_attention",
+    "pkv_varlen_prefill_attention_noalloc",
     "pkv_last_error",
     "pkv_version",
     "pkv_bm_create",
@@ -115,6 +116,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pkv_varlen_prefill_attention.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
                                                  i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.pkv_varlen_prefill_attention.restype = ctypes.c_int
+    lib.pkv_varlen_prefill_attention_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i32,
+                                                         i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.pkv_varlen_prefill_attention_noalloc.restype = ctypes.c_int
     _declare_block_manager(lib)
     lib.pkv_last_error.argtypes = []
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -291,3 +295,32 @@ def varlen_prefill_attention(out: torch.Tensor, q: torch.Tensor, k_cache: torch.
         _ptr(block_tables), ns, total_q, max_seqlen_q, max_seqlen_k, hq, hkv, d, block_size,
         block_tables.shape[1], float(scale), 1 if causal else 0, _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+# PKV_PREFILL_NOALLOC_SCRATCH_BYTES of pagedkv.h: the fixed per-GPU scratch of the
+# allocation-free prefill entry point
+PREFILL_NOALLOC_SCRATCH_BYTES = 2 << 20
+
+
+def varlen_prefill_attention_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                     v_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                     cu_seqlens_k: torch.Tensor, block_tables: torch.Tensor,
+                                     max_seqlen_q: int, max_seqlen_k: int, block_size: int,
+                                     scale: float, causal: bool = True, stream=None) -> None:
+    """varlen_prefill_attention on the library's fixed per-GPU scratch (allocates nothing;
+    overlapping calls on one GPU race)."""
+    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, torch.bfloat16, name, 3)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        _need(t, torch.int32, name, 1)
+    _need(block_tables, torch.int32, "block_tables", 2)
+    total_q, hq, d = q.shape
+    hkv = k_cache.shape[1]
+    ns = cu_seqlens_q.shape[0] - 1
+    if out.shape != q.shape or k_cache.shape[2] != d or v_cache.shape != k_cache.shape \
+            or cu_seqlens_k.shape[0] != ns + 1 or block_tables.shape[0] != ns:
+        raise ValueError("varlen_prefill_attention_noalloc: inconsistent shapes")
+    _check(load().pkv_varlen_prefill_attention_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        _ptr(block_tables), ns, total_q, max_seqlen_q, max_seqlen_k, hq, hkv, d, block_size,
+        block_tables.shape[1], float(scale), 1 if causal else 0, _stream(stream)))

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -70,6 +71,41 @@ int32_t resolve_split(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, i
 int32_t num_splits(int32_t max_ctx, int32_t split) {
   const int32_t n = (max_ctx + split - 1) / split;
   return n < 1 ? 1 : n;
+}
+
+// Scratch of pkv_varlen_prefill_attention_noalloc: the prefill work list and
+// queue counters that pkv_varlen_prefill_attention keeps in the caller's
+// workspace, in a fixed array of device memory.  Each GPU the library runs on
+// holds its own copy until the process ends; host code reaches it only through
+// the device address looked up once per device (the array's name is not a
+// device address in host code).
+constexpr size_t kScratchBytes = PKV_PREFILL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there, with that device current).
+pkv_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "device %d beyond the %d devices the static scratch serves", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
 }
 
 }  // namespace
@@ -335,6 +371,34 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
   a.total_q = total_q;
   return hip_status(pkv::launch_varlen_prefill(a, workspace, static_cast<hipStream_t>(stream)),
                     "varlen_prefill_attention launch");
+}
+
+pkv_status pkv_varlen_prefill_attention_noalloc(void* out, const void* q, const void* k_cache,
+                                                const void* v_cache, const int32_t* cu_seqlens_q,
+                                                const int32_t* cu_seqlens_k,
+                                                const int32_t* block_tables, int32_t num_seqs,
+                                                int64_t total_q, int32_t max_seqlen_q,
+                                                int32_t max_seqlen_k, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t max_blocks_per_seq,
+                                                float scale, int32_t causal, void* stream) {
+  const size_t need = pkv_prefill_workspace_bytes(num_seqs, total_q, num_q_heads, num_kv_heads);
+  void* ws = nullptr;
+  if (need != SIZE_MAX && need > 0 && max_seqlen_q > 0) {
+    if (need > kScratchBytes)
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "this batch needs %zu bytes of prefill scratch; the static scratch holds %zu "
+                  "(pass a workspace to pkv_varlen_prefill_attention instead)",
+                  need, kScratchBytes);
+    const pkv_status st = scratch_ptr(&ws);
+    if (st != PKV_OK) return st;
+  }
+  // the same checks and kernels as the workspace entry point, on the scratch
+  return pkv_varlen_prefill_attention(out, q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
+                                      block_tables, num_seqs, total_q, max_seqlen_q, max_seqlen_k,
+                                      num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks_per_seq, scale, causal, ws,
+                                      ws ? kScratchBytes : 0, stream);
 }
 
 }  // extern "C"

@@ -148,3 +148,23 @@ def test_binding_rejects_host_tensors(lib):
     x = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pkv.store_kvcache(x, x, x, x, torch.zeros(2, dtype=torch.int32))
+
+
+def test_noalloc_prefill_scratch_limit(lib):
+    """The allocation-free prefill refuses, on the host, a batch whose work list does not
+    fit its fixed scratch (nothing is enqueued: the pointers are never touched), and the
+    header's size is the binding's."""
+    text = open(HEADER).read()
+    assert "#define PKV_PREFILL_NOALLOC_SCRATCH_BYTES ((size_t)2 << 20)" in text
+    assert binding.PREFILL_NOALLOC_SCRATCH_BYTES == 2 << 20
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced
+    big = 8 << 20                   # 8M query rows: ~65k (sequence, tile) pairs
+    need = lib.pkv_prefill_workspace_bytes(64, big, 32, 8)
+    assert need > binding.PREFILL_NOALLOC_SCRATCH_BYTES
+    st = lib.pkv_varlen_prefill_attention_noalloc(fake, fake, fake, fake, fake, fake, fake, 64, big,
+                                                  1024, 1024, 32, 8, 128, 256, 4, 0.1, 1, None)
+    assert st == binding.PKV_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.pkv_last_error()
+    # empty batches are no-ops that never look the scratch up
+    assert lib.pkv_varlen_prefill_attention_noalloc(fake, fake, fake, fake, fake, fake, fake, 0, 0,
+                                                    0, 0, 32, 8, 128, 256, 4, 0.1, 1, None) == 0
