@@ -233,8 +233,8 @@ pkv_status pkv_varlen_prefill_attention(void* out, const void* q, const void* k_
  * which each GPU the library runs on holds from the first call there until
  * the process ends.  Batches whose pkv_prefill_workspace_bytes(...) exceeds
  * that size are refused with PKV_ERR_UNSUPPORTED before anything is enqueued
- * (about 32,000 (sequence, 128-row query tile) pairs at 4 query heads per kv
- * head).  Every call on one GPU uses that GPU's one array: calls that may
+ * (about 32,000 (sequence, query tile) pairs: some 1 million query rows at
+ * 4 query heads per kv head, whose tiles hold 32 rows).  Every call on one GPU uses that GPU's one array: calls that may
  * overlap in time on one GPU (different streams, different host threads) race
  * and must not be issued; each call rewrites the array from the start, so
  * stale contents from an earlier call do not matter.  Arguments as for
