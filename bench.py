@@ -316,6 +316,120 @@ def run_sampling(args, torch, pkv, dev):
     print(json.dumps(rec), flush=True)
 
 
+# ---- decode steps replayed from captured graphs, against eager launches --------------------
+GRAPH_SWEEP = "graph_sweep"
+GRAPH_BATCHES = (1, 4, 16, 64, 256, 512)
+
+
+def run_graph_sweep(args, torch, pkv, dev):
+    """The decode step (the new tokens' store, then decode attention) at several batch
+    sizes with the batch-256 decode's shape (Hq 16, Hkv 8, d 128, contexts U[100,1024]),
+    four ways: two eager launches, the fused kernel eager, and each of those captured
+    once per input copy as a HIP graph and replayed.  Each figure is the average ms per
+    step over K back-to-back steps between two HIP events."""
+    import workload as W
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_harness as H
+    out = {}
+    for b in GRAPH_BATCHES:
+        seed = 4300 + b
+        rng = np.random.Generator(np.random.PCG64(seed))
+        ctx = rng.integers(100, 1024, size=b, endpoint=True)
+        w = W.decode(ctx, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+                     id_mode="choice", max_blocks_per_seq=4, seed=seed, rng=rng, name=f"decode_b{b}")
+        reps = max(1, min(4, math.ceil(2.0e9 / unique_step_bytes(w))))
+        copies = [w.materialize(dev) for _ in range(reps)]
+        outs = [torch.empty_like(c["q"]) for c in copies]
+        ws = torch.empty(max(16, pkv.decode_workspace_bytes(b, 16, 8, 128, w.max_context_len, 0)),
+                         dtype=torch.uint8, device=dev)
+
+        def two(i):
+            c = copies[i % reps]
+            pkv.store_kvcache(c["k_new"], c["v_new"], c["k_cache"], c["v_cache"], c["slot_mapping"])
+            pkv.paged_decode_attention(outs[i % reps], c["q"], c["k_cache"], c["v_cache"],
+                                       c["block_tables"], c["context_lens"], w.block_size,
+                                       w.max_context_len, w.scale, 0, ws)
+
+        def fused(i):
+            c = copies[i % reps]
+            pkv.store_and_decode(outs[i % reps], c["q"], c["k_new"], c["v_new"], c["k_cache"],
+                                 c["v_cache"], c["slot_mapping"], c["block_tables"], c["context_lens"],
+                                 w.block_size, w.max_context_len, w.scale, 0, ws)
+
+        def capture(body):
+            gs = []
+            for i in range(reps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    body(i)
+                gs.append(g)
+            return gs
+
+        def timed(body):
+            for i in range(args.warmup):
+                body(i)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(args.steps):
+                body(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        rec = {"eager_ms": timed(two), "fused_ms": timed(fused)}
+        g2 = capture(two)
+        rec["graph_ms"] = timed(lambda i: g2[i % reps].replay())
+        gf = capture(fused)
+        rec["graph_fused_ms"] = timed(lambda i: gf[i % reps].replay())
+        H.check_against_oracle(w, outs[0], [int(np.argmax(w.lk))])
+        rec["input_copies_rotated"] = reps
+        out[str(b)] = rec
+        del copies, outs, ws, g2, gf
+        torch.cuda.empty_cache()
+    best = min(min(r["graph_ms"], r["graph_fused_ms"]) for r in out.values())
+    rec = {"metric": "decode step ms (store + decode), eager vs graph replay", "value": best,
+           "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": best, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": GRAPH_SWEEP, "batches": list(GRAPH_BATCHES), "num_q_heads": 16,
+                      "num_kv_heads": 8, "head_dim": 128, "context": "U[100,1024]"},
+           "sweep": out}
+    print(json.dumps(rec), flush=True)
+
+
+def summarize_graph_trace(trace_dir: str, per: int = 25) -> str:
+    """Step time, kernel busy time and idle time per batch and launch kind, from a
+    rocprofv3 kernel trace of `--workload graph_sweep` run with K + W = `per` steps."""
+    import csv
+    import glob
+    import statistics as st
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += [r for r in csv.DictReader(open(f)) if "pkv" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    kinds = ["eager", "fused", "graph", "graph_fused"]
+    dec = [i for i, r in enumerate(rows) if "paged_decode_kernel" in r["Kernel_Name"]]
+    if len(dec) != per * len(kinds) * len(GRAPH_BATCHES):
+        raise SystemExit(f"expected {per * len(kinds) * len(GRAPH_BATCHES)} decode dispatches, found {len(dec)}")
+    us = lambda a, b: (int(b) - int(a)) / 1e3
+    out = []
+    for bi, b in enumerate(GRAPH_BATCHES):
+        for ki, kind in enumerate(kinds):
+            seg = dec[(bi * 4 + ki) * per:(bi * 4 + ki + 1) * per][5:]  # after the warm-up steps
+            starts = [i - 1 if "store_kvcache" in rows[i - 1]["Kernel_Name"] else i for i in seg]
+            busy, span = [], []
+            for a, z in zip(starts, starts[1:]):
+                busy.append(sum(us(r["Start_Timestamp"], r["End_Timestamp"]) for r in rows[a:z]))
+                span.append(us(rows[a]["Start_Timestamp"], rows[z]["Start_Timestamp"]))
+            dd = [us(rows[i]["Start_Timestamp"], rows[i]["End_Timestamp"]) for i in seg]
+            out.append(f"B={b:4d} {kind:12s} step {st.mean(span):7.1f} us  kernels busy {st.mean(busy):7.1f} us  "
+                       f"idle {st.mean(span) - st.mean(busy):6.1f} us  decode kernel {st.median(dd):6.1f} us  "
+                       f"kernels/step {starts[1] - starts[0]}")
+    return "\n".join(out)
+
+
 # ---- GPU run ----------------------------------------------------------------------------
 def unique_step_bytes(w) -> int:
     """Bytes one step touches, each distinct byte once: Q, O, the K/V of every distinct
@@ -550,10 +664,16 @@ def main():
                     help="end with a 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into profiles/traffic_<workload>.json")
+    ap.add_argument("--graph-trace", metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 kernel trace of --workload graph_sweep "
+                         "(run with --steps 20 --warmup 5)")
     args = ap.parse_args()
 
     if args.counters:
         print(json.dumps(summarize_counters(args.workload, *args.counters)), flush=True)
+        return
+    if args.graph_trace:
+        print(summarize_graph_trace(args.graph_trace, args.steps + args.warmup), flush=True)
         return
 
     if args.gpus != 1:
@@ -572,6 +692,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == SAMPLE_WORKLOAD:
         run_sampling(args, torch, pkv, dev)
+        return
+    if args.workload == GRAPH_SWEEP:
+        run_graph_sweep(args, torch, pkv, dev)
         return
     single = args.workload is not None
     headline = args.workload or HEADLINE
