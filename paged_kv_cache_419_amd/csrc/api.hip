@@ -236,6 +236,9 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.split_tokens = split;
   a.n_split = n;
+  a.max_context_len = max_context_len;
+  a.order_shift = 0;
+  while ((max_context_len >> a.order_shift) > 255) ++a.order_shift;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.k_new = k_new;
   a.v_new = v_new;

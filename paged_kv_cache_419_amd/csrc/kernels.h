@@ -27,6 +27,8 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int32_t split_tokens;
   int32_t n_split;
+  int32_t max_context_len;
+  int32_t order_shift;  // max_context_len >> order_shift < 256: length classes of the work order
   float scale_log2;     // scale * log2(e)
   // Fused store (all null / 0 otherwise): the new token of sequence b is row b
   // of k_new / v_new; it is attended from there and written to cache slot

@@ -85,8 +85,9 @@ struct SeqView {
 constexpr int kPfWaveRows = kPfKeys / kPfWaves;
 
 // Block-table entry of this wave's rows of the tile starting at key k0 (a
-// scalar load; issued one tile ahead of its use).
-__device__ __forceinline__ int64_t tile_block(const SeqView& sv, int k0, int wave) {
+// scalar load, issued at the end of a tile step and used in the next one: kept
+// 32-bit until then, so nothing waits for it before the next step's barrier).
+__device__ __forceinline__ int32_t tile_block(const SeqView& sv, int k0, int wave) {
   return sv.bt[min(k0 + wave * kPfWaveRows, sv.lk - 1) >> sv.shift];
 }
 
@@ -175,30 +176,6 @@ struct WaveState {
   float m;                            // running reference max (log2 domain) of this lane's row
 };
 
-// Scheduling shape for a block of M MFMAs fed by NR LDS reads: the first
-// AHEAD reads go out before any MFMA, then each MFMA is followed by the next
-// reads (evenly spread), so AHEAD reads stay in flight and the matrix core
-// does not wait on LDS latency.
-template <int M, int NR, int AHEAD>
-__device__ __forceinline__ void sched_reads_ahead() {
-  static_assert(AHEAD <= NR, "more reads ahead than reads");
-  constexpr int kRest = NR - AHEAD;
-#pragma unroll
-  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  constexpr int kPer = (kRest + M - 1) / M > 0 ? (kRest + M - 1) / M : 1;
-  constexpr int kFull = kRest / kPer;  // MFMAs followed by kPer reads
-  constexpr int kRem = kRest % kPer;   // reads after MFMA number kFull
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < kFull) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);
-    } else if (i == kFull && kRem > 0) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kRem, 0);
-    }
-  }
-}
-
 // Weights exp2(s c - m) of one 64-key tile, rounded to bf16 and packed in
 // the B-operand order of the PV product: 16-key block u = 2 kb + hb, k-slots
 // 0..3 are keys 16u + 4h + i, k-slots 4..7 are keys 16u + 8 + 4h + i.
@@ -247,9 +224,16 @@ __device__ __forceinline__ float row_max_scaled(const f32x16 (&s)[kPfKB], float 
 }
 
 // One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// The next tile's loads (job) go out one after every kGap MFMAs of the S
-// product, so the waves of a CU do not all queue their loads on the memory
-// pipeline at once right after the barrier.
+//
+// The instruction order is fixed by hand with scheduling fences (the
+// compiler's own schedule waits for every LDS read right before the MFMA that
+// uses it): the K operands are read kReadAhead MFMAs ahead, the two 32-key
+// score blocks alternate so no MFMA waits on the one before it, and the next
+// tile's loads (job) go out one after every kGap MFMAs of the S product, so
+// the waves of a CU do not all queue their loads on the memory pipeline at
+// once right after the barrier.  The first V^T operands are read before the
+// softmax, so their latency hides behind it, and the rest stay kVAhead MFMAs
+// ahead of the PV product.
 template <int D>
 __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_bytes vt,
                                              const uint32_t (&kaddr)[PrefillShape<D>::KS],
@@ -258,25 +242,42 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
                                              float c, float masked, const DmaJob& job,
                                              const TileLoadOffsets<D>& lo) {
   using S = PrefillShape<D>;
-  constexpr int kGap = kPfKB * S::KS / (2 * S::LOADS);
-  static_assert(kGap >= 1 && kGap * 2 * S::LOADS == kPfKB * S::KS, "loads per MFMA slot");
+  static_assert(kPfKB == 2, "two interleaved score blocks");
+  constexpr int kNS = kPfKB * S::KS;  // MFMAs of the S product
+  constexpr int kNP = kPfU * S::DC;   // MFMAs of the PV product
+  constexpr int kGap = kNS / (2 * S::LOADS);
+  static_assert(kGap >= 1 && kGap * 2 * S::LOADS == kNS, "loads per MFMA slot");
+  constexpr int kReadAhead = 3;
+  constexpr int kVAhead = 4;
+  static_assert(kReadAhead < kNS && kVAhead <= kNP, "read-ahead depth");
+
+  u32x4 ka[kNS];
+  auto kread = [&](int i) {  // operand of S MFMA i: key block i % 2, k-step i / 2
+    ka[i] = *(const lds_u32x4*)(kt + kaddr[i >> 1] + (i & 1) * 32 * S::ROWB);
+  };
+  uint2 vlo[kNP], vhi[kNP];
+  auto vread = [&](int j) {  // operand of PV MFMA j: 16-key block j / DC, d block j % DC
+    const int u = j / S::DC, cb = j % S::DC;
+    vlo[j] = lds_read_tr16(vt + vaddr[cb] + 16 * u * S::ROWB);
+    vhi[j] = lds_read_tr16(vt + vaddr[cb] + (16 * u + 8) * S::ROWB);
+  };
+
   f32x16 s[kPfKB];
 #pragma unroll
-  for (int kb = 0; kb < kPfKB; ++kb) {
-    s[kb] = f32x16{};
+  for (int i = 0; i < kReadAhead; ++i) kread(i);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      const u32x4 a = *(const lds_u32x4*)(kt + kaddr[ks] + kb * 32 * S::ROWB);
-      s[kb] = mfma32x32x16(a, w.qb[ks], s[kb]);
-      const int i = kb * S::KS + ks;
-      if (i % kGap == kGap - 1) dma_one<D>(job, lo, i / kGap);
-    }
+  for (int i = 0; i < kNS; ++i) {
+    if (i + kReadAhead < kNS) kread(i + kReadAhead);
+    const int kb = i & 1, ks = i >> 1;
+    s[kb] = mfma32x32x16(ka[i], w.qb[ks], ks == 0 ? f32x16{} : s[kb]);
+    if (i % kGap == kGap - 1) dma_one<D>(job, lo, i / kGap);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // Keep K operand reads in flight ahead of the MFMAs (LDS latency is a few
-  // MFMA issue slots).  Two ahead here and six for the V reads below were the
-  // fastest of 1-8 and 4-16 measured (deeper read-ahead holds more registers
-  // and crowds the next tile's loads).
-  sched_reads_ahead<kPfKB * S::KS, kPfKB * S::KS, 2>();
+#pragma unroll
+  for (int j = 0; j < kVAhead; ++j) vread(j);
+  __builtin_amdgcn_sched_barrier(0);
+
   // element 4j + i of s[kb] is key k0 + 32 kb + 8 j + 4 h + i of this lane's row
   if (need_mask) {
 #pragma unroll
@@ -306,22 +307,17 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
     tsum = tile_weights(s, pb, w.m, c);
   }
   w.lsum += tsum;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < kPfU; ++u) {
-#pragma unroll
-    for (int cb = 0; cb < S::DC; ++cb) {
-      const uint2 lo = lds_read_tr16(vt + vaddr[cb] + 16 * u * S::ROWB);
-      const uint2 hi = lds_read_tr16(vt + vaddr[cb] + (16 * u + 8) * S::ROWB);
-      w.o[cb] = mfma32x32x16(u32x4{lo.x, lo.y, hi.x, hi.y}, pb[u], w.o[cb]);
-    }
+  for (int j = 0; j < kNP; ++j) {
+    if (j + kVAhead < kNP) vread(j + kVAhead);
+    const int u = j / S::DC, cb = j % S::DC;
+    w.o[cb] = mfma32x32x16(u32x4{vlo[j].x, vlo[j].y, vhi[j].x, vhi[j].y}, pb[u], w.o[cb]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  sched_reads_ahead<kPfU * S::DC, 2 * kPfU * S::DC, 6>();
 }
 
-// Start of tile step t: wait for this wave's loads of tile t (younger tiles
-// stay in flight) and for its LDS reads of tile t - 1, sync the workgroup,
-// then issue tile t + kPfStages - 1 into the slot tile t - 1 has just freed.
-// blk_next carries the block-table entry of that tile, looked up a step ahead.
+// LDS slot of ring position t: a K tile followed by a V tile.
 template <int D>
 __device__ __forceinline__ lds_bytes kslot_of(lds_bytes lbase, int t) {
   return lbase + (t % kPfStages) * (2 * PrefillShape<D>::TILE);
@@ -329,29 +325,6 @@ __device__ __forceinline__ lds_bytes kslot_of(lds_bytes lbase, int t) {
 template <int D>
 __device__ __forceinline__ lds_bytes vslot_of(lds_bytes lbase, int t) {
   return kslot_of<D>(lbase, t) + PrefillShape<D>::TILE;
-}
-
-template <int D>
-__device__ __forceinline__ void tile_sync(int t, int n_tiles) {
-  using S = PrefillShape<D>;
-  switch (min(n_tiles - 1 - t, kPfStages - 2)) {  // tiles younger than t in flight
-    case 2: barrier_after_loads<2 * 2 * S::LOADS>(); break;
-    case 1: barrier_after_loads<1 * 2 * S::LOADS>(); break;
-    default: barrier_after_loads<0>(); break;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void tile_sync_and_issue(const SeqView& sv, int t, int n_tiles, int wave,
-                                                    const TileLoadOffsets<D>& lo,
-                                                    int64_t& blk_next, lds_bytes lbase) {
-  tile_sync<D>(t, n_tiles);
-  const int tn = t + kPfStages - 1;
-  if (tn < n_tiles) {
-    dma_all<D>(dma_job<D>(sv, blk_next, tn * kPfKeys, wave, true, kslot_of<D>(lbase, tn),
-                          vslot_of<D>(lbase, tn)), lo);
-    if (tn + 1 < n_tiles) blk_next = tile_block(sv, (tn + 1) * kPfKeys, wave);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -660,13 +633,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
         barrier_after_vm<0>();
       }
     };
-    int64_t blk_next = n_eff > 1 ? tile_block(sv, kPfKeys, wave) : 0;
+    int32_t blk_next = n_eff > 1 ? tile_block(sv, kPfKeys, wave) : 0;
     auto inner_step = [&](int t) -> DmaJob {  // loads of tile t + 1
       sync_step(t);
-      const DmaJob job = dma_job<D>(sv, blk_next, (t + 1) * kPfKeys, wave, t + 1 < n_tiles, kslot(T + 1),
-                                    vslot(T + 1));
+      return dma_job<D>(sv, blk_next, (t + 1) * kPfKeys, wave, t + 1 < n_tiles, kslot(T + 1), vslot(T + 1));
+    };
+    auto next_block = [&](int t) {  // block-table entry of tile t + 2, for the next step
       if (t + 2 < n_eff) blk_next = tile_block(sv, (t + 2) * kPfKeys, wave);
-      return job;
     };
 
     const int n_inner = n_eff - 1;
@@ -676,9 +649,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
       const DmaJob job = inner_step(t);
       const int k0 = t * kPfKeys;
       compute_tile<D>(w, kslot(T), vslot(T), kaddr, vaddr, k0, lim, k0 + kPfKeys - 1 > lim_lo, h, c, masked, job, lo);
+      next_block(t);
     }
 #pragma unroll 1
-    for (; t < n_inner; ++t, ++T) dma_all<D>(inner_step(t), lo);
+    for (; t < n_inner; ++t, ++T) {
+      dma_all<D>(inner_step(t), lo);
+      next_block(t);
+    }
 
     // Last ring step of the item: the loads that follow are the next item's
     // tile 0 (none after the last item, whose step then fetches nothing).
