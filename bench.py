@@ -339,7 +339,7 @@ def run_graph_sweep(args, torch, pkv, dev):
                      id_mode="choice", max_blocks_per_seq=4, seed=seed, rng=rng, name=f"decode_b{b}")
         reps = max(1, min(4, math.ceil(2.0e9 / unique_step_bytes(w))))
         copies = [w.materialize(dev) for _ in range(reps)]
-        outs = [torch.empty_like(c["q"]) for c in copies]
+        outs = [torch.full_like(c["q"], float("nan")) for c in copies]
         ws = torch.empty(max(16, pkv.decode_workspace_bytes(b, 16, 8, 128, w.max_context_len, 0)),
                          dtype=torch.uint8, device=dev)
 
@@ -493,7 +493,7 @@ def measure(name, args, torch, pkv, dev, pool, cpu_budget):
     decode = w.kind == "decode"
     reps = args.replicas or max(1, min(4, math.ceil(2.0e9 / unique_step_bytes(w))))
     copies = [w.materialize(dev) for _ in range(reps)]
-    outs = [torch.empty_like(c["q"]) for c in copies]
+    outs = [torch.full_like(c["q"], float("nan")) for c in copies]
     split = args.split_tokens
     ws_bytes = (pkv.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                            w.max_context_len, split) if decode else

@@ -17,7 +17,8 @@ def gpu_step(w, split_tokens: int = 0, tensors=None, store: bool = True):
     t = w.materialize("cuda") if tensors is None else tensors
     if store:
         pkv.store_kvcache(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
-    out = torch.empty_like(t["q"])
+    # NaN everywhere first: a row the kernels never write fails the comparison
+    out = torch.full_like(t["q"], float("nan"))
     if w.kind == "decode":
         pkv.paged_decode_attention(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                                    t["context_lens"], w.block_size, w.max_context_len, w.scale,

@@ -67,7 +67,7 @@ def prefill(bm, cache, ids, prompts, cached):
     bt = bm.tables(ids)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     pkv.store_kvcache(k_new, v_new, cache.k, cache.v, dev(slots))
-    out = torch.empty_like(q)
+    out = torch.full_like(q, float("nan"))
     pkv.varlen_prefill_attention(out, q, cache.k, cache.v, dev(cu_q), dev(cu_k), dev(bt),
                                  int(np.diff(cu_q).max()), int(np.diff(cu_k).max()), BS, SCALE, True)
     torch.cuda.synchronize()
@@ -90,7 +90,7 @@ def decode_step(bm, cache, ids, seqs, step):
     ctx = np.asarray([p + 1 for p in pos], np.int32)
     bt = bm.tables(ids)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    out = torch.empty_like(q)
+    out = torch.full_like(q, float("nan"))
     max_ctx = bt.shape[1] * BS
     pkv.store_and_decode(out, q, kn, vn, cache.k, cache.v, dev(slots), dev(bt), dev(ctx), BS, max_ctx,
                          SCALE)

@@ -45,7 +45,7 @@ def _per_sequence(w, t):
 def _check(w, split, seqs):
     te = w.materialize("cuda")
     pkv.store_kvcache(te["k_new"], te["v_new"], te["k_cache"], te["v_cache"], te["slot_mapping"])
-    ref = torch.empty_like(te["q"])
+    ref = torch.full_like(te["q"], float("nan"))
     pkv.paged_decode_attention(ref, te["q"], te["k_cache"], te["v_cache"], te["block_tables"],
                                te["context_lens"], w.block_size, w.max_context_len, w.scale, split)
     torch.cuda.synchronize()
@@ -53,7 +53,7 @@ def _check(w, split, seqs):
     del te
     tf = w.materialize("cuda")
     kn, vn, sm = _per_sequence(w, tf)
-    out = torch.empty_like(tf["q"])
+    out = torch.full_like(tf["q"], float("nan"))
     pkv.store_and_decode(out, tf["q"], kn, vn, tf["k_cache"], tf["v_cache"], sm, tf["block_tables"],
                          tf["context_lens"], w.block_size, w.max_context_len, w.scale, split)
     torch.cuda.synchronize()

@@ -25,7 +25,7 @@ def _note(msg):
 
 def _eager(w, t, out_rows, split):
     pkv.store_kvcache(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
-    out = torch.empty_like(t["q"])
+    out = torch.full_like(t["q"], float("nan"))
     pkv.paged_decode_attention(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                                t["context_lens"], w.block_size, out_rows, w.scale, split)
     return out
@@ -108,7 +108,7 @@ def test_fused_graph_replays_match_eager_fused_call():
         idx = torch.tensor(seqs, device="cuda")
         tin = {k: (te[k][idx] if k in ("q", "k_new", "v_new", "slot_mapping", "block_tables",
                                         "context_lens") else te[k]) for k in te}
-        ref = torch.empty_like(tin["q"])
+        ref = torch.full_like(tin["q"], float("nan"))
         pkv.store_and_decode(ref, tin["q"], tin["k_new"], tin["v_new"], te["k_cache"], te["v_cache"],
                              tin["slot_mapping"], tin["block_tables"], tin["context_lens"],
                              w.block_size, max_ctx, w.scale)
