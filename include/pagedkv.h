@@ -117,10 +117,13 @@ int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_
  *   q             device bf16 [batch, num_q_heads, head_dim]
  *   block_tables  device int32 [batch, max_blocks_per_seq]; entries past a
  *                 sequence's last block are ignored (-1 by convention)
- *   context_lens  device int32 [batch]
+ *   context_lens  device int32 [batch]; a value outside [0, max_context_len]
+ *                 is taken as the nearest end of that range
  *   max_context_len  host-side bound: context_lens[b] <= max_context_len <=
  *                 max_blocks_per_seq * block_size (sizes the launch; no device
- *                 read).  Tokens beyond it are never visited.
+ *                 read).  Tokens beyond it are never visited.  Workgroups take
+ *                 the sequences longest first (the result does not depend on
+ *                 the order).
  *   split_tokens  context tokens per workgroup: 0 = automatic, else a positive
  *                 multiple of 32.  Sequences longer than one split are
  *                 processed in several workgroups whose partial softmax states

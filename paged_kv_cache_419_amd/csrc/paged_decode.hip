@@ -229,55 +229,81 @@ __device__ __forceinline__ int workgroup_inclusive_sum(int v, int* part) {
   return v;
 }
 
-// Sequence at place r of the batch in work order: by context length, longest
-// first, in length classes of 2^order_shift tokens (at most 256 classes),
-// batch order inside a class.  Every workgroup derives the same order from
-// context_lens: a histogram of the classes, a prefix sum that finds the class
-// holding place r, and a prefix count that finds the sequence inside it.
-// Long sequences then start first and the short ones fill the end of the
-// launch, so no CU is left with one long sequence after the others are done.
-__device__ int sequence_in_work_order(const DecodeArgs& a, int r) {
-  static_assert(kDecThreads == 256, "one thread per length class");
-  __shared__ int hist[256];
+// Sequence at place r of the batch in work order, and its context length:
+// by context length, longest first, in length classes of 2^order_shift
+// tokens (at most 256 classes), batch order inside a class.  Every workgroup
+// derives the same order from context_lens: a histogram of the classes, a
+// prefix sum that finds the class holding place r, and a prefix count that
+// finds the sequence inside it.  Long sequences then start first and the
+// short ones fill the end of the launch, so no CU is left with one long
+// sequence after the others are done.  context_lens is read once (the
+// workgroup needs its sequence's length anyway): up to kHeld lengths per
+// thread stay in registers, larger batches read theirs again.  Lengths are
+// clamped to [0, max_context_len].
+struct SeqPick {
+  int b;
+  int ctx;
+};
+
+__device__ SeqPick sequence_in_work_order(const DecodeArgs& a, int r) {
+  constexpr int kClasses = 256;
+  constexpr int kPerThread = kClasses / kDecThreads;  // consecutive classes of one thread
+  static_assert(kPerThread * kDecThreads == kClasses, "classes split evenly over the threads");
+  constexpr int kHeld = 4;
+  __shared__ int hist[kClasses];
   __shared__ int part[kDecWaves];
-  __shared__ int pick[3];
+  __shared__ int pick[4];
   const int tid = threadIdx.x;
   const int per = (a.batch + kDecThreads - 1) / kDecThreads;  // sequences of this thread: a range
   const int j0 = tid * per;
   const int j1 = min(j0 + per, a.batch);
-  auto cls = [&](int j) {  // 0 for the longest class
-    const int c = min(max(a.context_lens[j], 0), a.max_context_len);
-    return 255 - (c >> a.order_shift);
-  };
-  hist[tid] = 0;
+  auto len_at = [&](int j) { return min(max(a.context_lens[j], 0), a.max_context_len); };
+  auto cls_of = [&](int len) { return 255 - (len >> a.order_shift); };  // 0 for the longest class
+  int held[kHeld];
+#pragma unroll
+  for (int e = 0; e < kHeld; ++e) held[e] = j0 + e < j1 ? len_at(j0 + e) : 0;
+  auto len_of = [&](int j) { return j - j0 < kHeld ? held[j - j0] : len_at(j); };
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) hist[tid * kPerThread + k] = 0;
   __syncthreads();
-  for (int j = j0; j < j1; ++j) atomicAdd(&hist[cls(j)], 1);
+  for (int j = j0; j < j1; ++j) atomicAdd(&hist[cls_of(len_of(j))], 1);
   __syncthreads();
-  const int cnt = hist[tid];
-  const int end = workgroup_inclusive_sum(cnt, part);
-  if (r >= end - cnt && r < end) {
-    pick[0] = tid;
-    pick[1] = r - (end - cnt);
+  int cnt[kPerThread], own = 0;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) own += cnt[k] = hist[tid * kPerThread + k];
+  int run = workgroup_inclusive_sum(own, part) - own;  // places before this thread's classes
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    if (r >= run && r < run + cnt[k]) {
+      pick[0] = tid * kPerThread + k;
+      pick[1] = r - run;
+    }
+    run += cnt[k];
   }
   __syncthreads();
   const int want = pick[0], rank = pick[1];
   int mine = 0;
-  for (int j = j0; j < j1; ++j) mine += cls(j) == want;
+  for (int j = j0; j < j1; ++j) mine += cls_of(len_of(j)) == want;
   const int upto = workgroup_inclusive_sum(mine, part);
   if (rank >= upto - mine && rank < upto) {
     int k = rank - (upto - mine);
     for (int j = j0; j < j1; ++j) {
-      if (cls(j) == want) {
-        if (k == 0) pick[2] = j;
+      const int len = len_of(j);
+      if (cls_of(len) == want) {
+        if (k == 0) {
+          pick[2] = j;
+          pick[3] = len;
+        }
         --k;
       }
     }
   }
   __syncthreads();
-  return pick[2];
+  return SeqPick{pick[2], pick[3]};
 }
 
 template <int D>
+// (second bound: at least two waves per SIMD, i.e. up to 256 registers per lane)
 __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS];
@@ -295,7 +321,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs
   const int split = static_cast<int>(lin / pairs);
   const int64_t pair = lin - split * pairs;
   const int gy = static_cast<int>(pair / a.batch);
-  const int b = __builtin_amdgcn_readfirstlane(sequence_in_work_order(a, static_cast<int>(pair % a.batch)));
+  const SeqPick sp = sequence_in_work_order(a, static_cast<int>(pair % a.batch));
+  const int b = __builtin_amdgcn_readfirstlane(sp.b);
   const int g = gy / a.head_groups;
   const int hg = gy - g * a.head_groups;
   const int lane = threadIdx.x & (kWave - 1);
@@ -303,7 +330,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
 
-  const int ctx = a.context_lens[b];
+  const int ctx = __builtin_amdgcn_readfirstlane(sp.ctx);
   const int t0 = split * a.split_tokens;
   const int heads_here = min(16, a.group - hg * 16);
   const int h0 = g * a.group + hg * 16;
@@ -451,7 +478,7 @@ __global__ __launch_bounds__(D) void paged_decode_combine_kernel(DecodeArgs a) {
   const int h = static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.num_q_heads));
   const int b = static_cast<int>(blockIdx.x / static_cast<uint32_t>(a.num_q_heads));
   const int d = threadIdx.x;
-  const int ctx = a.context_lens[b];
+  const int ctx = min(max(a.context_lens[b], 0), a.max_context_len);  // as the split kernel takes it
   const int n = min(a.n_split, (ctx + a.split_tokens - 1) / a.split_tokens);
   const int64_t base = (static_cast<int64_t>(b) * a.num_q_heads + h) * a.n_split;
   float M = -INFINITY;

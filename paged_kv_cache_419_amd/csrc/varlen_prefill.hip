@@ -377,17 +377,37 @@ __device__ __forceinline__ int32_t block_entry(const PrefillArgs& a, int seq, in
 
 // Lists the pairs into the workspace (at most `cap` of them: the bound the
 // workspace was sized for, which holds when cu_seqlens_q ends at total_q) and
-// clears the queue counters.
+// clears the queue counters.  Batches of up to 1024 sequences are listed
+// longest first (by key count, ties in batch order), each sequence's q tiles
+// together: the long items start first and short ones fill the end of the
+// launch (~4 % faster at 64 sequences of 100-1024 tokens than batch order);
+// larger batches keep batch order.
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32_t rows_per_wg,
                                                             int32_t cap, int* ws) {
   __shared__ int s_incl[1024];
+  __shared__ int s_order[1024];  // place -> sequence, when sorted
   __shared__ int s_total;
   const int tid = threadIdx.x;
   if (tid < kWsCountersInts) ws[tid] = 0;
   if (tid == 0) s_total = 0;
+  const bool sorted = a.num_seqs <= 1024;
+  if (sorted) {
+    const int lk = tid < a.num_seqs ? a.cu_k[tid + 1] - a.cu_k[tid] : -1;
+    s_incl[tid] = lk;
+    __syncthreads();
+    if (tid < a.num_seqs) {
+      int place = 0;
+      for (int j = 0; j < a.num_seqs; ++j) {
+        const int o = s_incl[j];
+        place += (o > lk) || (o == lk && j < tid);
+      }
+      s_order[place] = tid;
+    }
+  }
   __syncthreads();
+  auto seq_at = [&](int i) { return sorted ? s_order[i] : i; };
   for (int s0 = 0; s0 < a.num_seqs; s0 += 1024) {
-    const int s = s0 + tid;
+    const int s = s0 + tid < a.num_seqs ? seq_at(s0 + tid) : a.num_seqs;
     const int lq = s < a.num_seqs ? a.cu_q[s + 1] - a.cu_q[s] : 0;
     const int nqt = lq > 0 ? (lq + rows_per_wg - 1) / rows_per_wg : 0;
     s_incl[tid] = nqt;
@@ -407,7 +427,7 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32
         const int mid = (lo + hi) >> 1;
         if (s_incl[mid] > r) hi = mid; else lo = mid + 1;
       }
-      const int seq = s0 + lo;
+      const int seq = seq_at(s0 + lo);
       const int first = s_incl[lo] - (lo > 0 ? s_incl[lo - 1] : 0);  // pairs of seq
       const int rank = r - (s_incl[lo] - first);
       const int q_start = a.cu_q[seq];
