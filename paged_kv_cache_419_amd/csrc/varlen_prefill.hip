@@ -380,22 +380,40 @@ __device__ __forceinline__ int32_t block_entry(const PrefillArgs& a, int seq, in
 // clears the queue counters.  Batches of up to 1024 sequences are listed
 // longest first (by key count, ties in batch order), each sequence's q tiles
 // together: the long items start first and short ones fill the end of the
-// launch (~4 % faster at 64 sequences of 100-1024 tokens than batch order);
-// larger batches keep batch order.
+// launch (~1.5 % faster at 64 sequences of 100-1024 tokens than batch
+// order); their cu_seqlens and block-table entries are read once, all at
+// the start, into LDS.  Larger batches keep batch order and read them where
+// they are needed.
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32_t rows_per_wg,
                                                             int32_t cap, int* ws) {
+  constexpr int kStaged = 1024;
   __shared__ int s_incl[1024];
-  __shared__ int s_order[1024];  // place -> sequence, when sorted
+  __shared__ int s_order[kStaged];  // place -> sequence, when staged
+  __shared__ int4 s_seq[kStaged];   // q start, Lq, Lk of each sequence, when staged
+  __shared__ int4 s_blk[kStaged];   // block-table entries of key rows 0, 16, 32, 48
   __shared__ int s_total;
   const int tid = threadIdx.x;
   if (tid < kWsCountersInts) ws[tid] = 0;
   if (tid == 0) s_total = 0;
-  const bool sorted = a.num_seqs <= 1024;
-  if (sorted) {
-    const int lk = tid < a.num_seqs ? a.cu_k[tid + 1] - a.cu_k[tid] : -1;
-    s_incl[tid] = lk;
+  const bool staged = a.num_seqs <= kStaged;
+  auto seq_of = [&](int s) {
+    const int q0 = a.cu_q[s];
+    return int4{q0, a.cu_q[s + 1] - q0, a.cu_k[s + 1] - a.cu_k[s], 0};
+  };
+  auto blk_of = [&](int s) {
+    return int4{block_entry(a, s, 0 * kPfWaveRows), block_entry(a, s, 1 * kPfWaveRows),
+                block_entry(a, s, 2 * kPfWaveRows), block_entry(a, s, 3 * kPfWaveRows)};
+  };
+  if (staged) {
+    if (tid < a.num_seqs) {
+      const int4 sq = seq_of(tid);
+      s_seq[tid] = sq;
+      s_blk[tid] = blk_of(tid);
+      s_incl[tid] = sq.z;
+    }
     __syncthreads();
     if (tid < a.num_seqs) {
+      const int lk = s_incl[tid];
       int place = 0;
       for (int j = 0; j < a.num_seqs; ++j) {
         const int o = s_incl[j];
@@ -405,10 +423,11 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32
     }
   }
   __syncthreads();
-  auto seq_at = [&](int i) { return sorted ? s_order[i] : i; };
+  auto seq_at = [&](int i) { return staged ? s_order[i] : i; };
+  auto info = [&](int s) { return staged ? s_seq[s] : seq_of(s); };
   for (int s0 = 0; s0 < a.num_seqs; s0 += 1024) {
     const int s = s0 + tid < a.num_seqs ? seq_at(s0 + tid) : a.num_seqs;
-    const int lq = s < a.num_seqs ? a.cu_q[s + 1] - a.cu_q[s] : 0;
+    const int lq = s < a.num_seqs ? info(s).y : 0;
     const int nqt = lq > 0 ? (lq + rows_per_wg - 1) / rows_per_wg : 0;
     s_incl[tid] = nqt;
     __syncthreads();
@@ -430,13 +449,12 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32
       const int seq = seq_at(s0 + lo);
       const int first = s_incl[lo] - (lo > 0 ? s_incl[lo - 1] : 0);  // pairs of seq
       const int rank = r - (s_incl[lo] - first);
-      const int q_start = a.cu_q[seq];
-      const int slq = a.cu_q[seq + 1] - q_start;
+      const int4 sq = info(seq);
+      const int4 bk = staged ? s_blk[seq] : blk_of(seq);
       int4* rec = reinterpret_cast<int4*>(ws + kWsRecsInt + static_cast<int64_t>(base + r) * kRecInts);
-      rec[0] = int4{seq, first - 1 - rank, q_start, slq};
-      rec[1] = int4{a.cu_k[seq + 1] - a.cu_k[seq], block_entry(a, seq, 0 * kPfWaveRows),
-                    block_entry(a, seq, 1 * kPfWaveRows), block_entry(a, seq, 2 * kPfWaveRows)};
-      rec[2] = int4{block_entry(a, seq, 3 * kPfWaveRows), 0, 0, 0};
+      rec[0] = int4{seq, first - 1 - rank, sq.x, sq.y};
+      rec[1] = int4{sq.z, bk.x, bk.y, bk.z};
+      rec[2] = int4{bk.w, 0, 0, 0};
     }
     __syncthreads();
     if (tid == 0) s_total = base + chunk;

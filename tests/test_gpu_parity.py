@@ -92,6 +92,32 @@ def test_decode_splits(name, split):
     assert ok, f"max abs {ea:.3e} rel {er:.3e}"
 
 
+@pytest.mark.parametrize("split", [0, 32])
+def test_decode_clamps_context_lens(split):
+    """A length above max_context_len is read as max_context_len and a negative one as 0
+    (a zero row); the other rows are untouched, and the work order the kernel derives from
+    the lengths does not change any result."""
+    _note(f"decode clamp split {split}")
+    w = cases.get("decode_edge_b4")  # contexts 1, 255, 256, 700; max 700
+    t = w.materialize("cuda")
+    pkv.store_kvcache(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+
+    def run(lens):
+        out = torch.full_like(t["q"], float("nan"))
+        pkv.paged_decode_attention(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                   torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                                   w.block_size, w.max_context_len, w.scale, split)
+        torch.cuda.synchronize()
+        return bf16_bits(out)
+
+    base = run([1, 255, 256, 700])
+    clamped = run([1, 255, 256, 700 + 333])
+    negative = run([-7, 255, 256, 700])
+    assert (clamped == base).all()
+    assert (negative[1:] == base[1:]).all()
+    assert (negative[0] == 0).all()
+
+
 def test_single_key_rows_exact():
     """Context 1 returns V exactly; so does causal prefill row 0 without history."""
     for name in ["decode_edge_b4", "decode_tiny_bs16"]:
