@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -80,13 +81,24 @@ CALL_SOURCES = {
 SHARED_SOURCES = ("common.h", "kernels.h")
 
 
-def kernel_sources_sha(call: str) -> str:
-    """Hash of the sources that define one call's kernels."""
-    h = hashlib.sha256()
+def source_code_text(text: str) -> str:
+    """C++ source without comments and blank lines (a comment edit keeps the hash)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
+def kernel_sources_sha(call: str, read=None) -> str:
+    """Hash of the code (comments left out) of the sources that define one call's
+    kernels; `read(name)` returns a source's text (default: the working tree)."""
     csrc = os.path.join(ROOT, "paged_kv_cache_419_amd", "csrc")
+    if read is None:
+        def read(name):
+            with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+                return fh.read()
+    h = hashlib.sha256()
     for f in sorted(CALL_SOURCES[call] + SHARED_SOURCES):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        h.update(f.encode() + source_code_text(read(f)).encode())
     return h.hexdigest()[:16]
 
 
@@ -448,7 +460,8 @@ def _pct(xs, q):
 def measure_ceilings(torch, dev, reps: int = 10) -> dict:
     """What plain library kernels reach on this machine, beside the published peaks: a
     2 GiB device-to-device copy (bytes read + written per second) and a bf16 GEMM of
-    8192^3 through torch (hipBLASLt), each the median of `reps` timed calls."""
+    8192^3 through torch (rocBLAS and hipBLASLt, the faster kept), each the median of
+    `reps` timed calls."""
     out = {}
     n = 2 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -474,11 +487,25 @@ def measure_ceilings(torch, dev, reps: int = 10) -> dict:
     ms = med_ms(lambda: dst.copy_(src))
     out["copy_gbs"] = 2 * n / (ms * 1e-3) / 1e9
     out["copy_frac_of_hbm_peak"] = out["copy_gbs"] / HBM_PEAK_GBS
-    ms = med_ms(lambda: torch.mm(a, b, out=c))
-    out["gemm_bf16_tflops"] = 2 * 8192 ** 3 / (ms * 1e-3) / 1e12
+    # both BLAS back ends torch can select on ROCm; the faster is the ceiling
+    backends = {}
+    prev = torch.backends.cuda.preferred_blas_library()
+    for name, lib in (("rocblas", "cublas"), ("hipblaslt", "cublaslt")):
+        try:
+            torch.backends.cuda.preferred_blas_library(lib)
+            ms = med_ms(lambda: torch.mm(a, b, out=c))
+            backends[name] = 2 * 8192 ** 3 / (ms * 1e-3) / 1e12
+        except RuntimeError as e:  # a back end this build lacks
+            backends[name] = f"unavailable: {e}"
+    torch.backends.cuda.preferred_blas_library(prev)
+    timed = {k: v for k, v in backends.items() if isinstance(v, float)}
+    best = max(timed, key=timed.get)
+    out["gemm_bf16_tflops"] = timed[best]
+    out["gemm_backend"] = best
+    out["gemm_bf16_tflops_by_backend"] = backends
     out["gemm_frac_of_mfma_peak"] = out["gemm_bf16_tflops"] / MFMA_BF16_PEAK_TFLOPS
     out["how"] = ("median of 10 event-timed calls: torch copy_ of 2 GiB (read + write bytes), "
-                  "torch.mm bf16 8192x8192x8192 (hipBLASLt)")
+                  "torch.mm bf16 8192x8192x8192 under rocBLAS and hipBLASLt, the faster kept")
     del src, dst, a, b, c
     torch.cuda.empty_cache()
     return out

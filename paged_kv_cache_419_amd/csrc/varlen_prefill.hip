@@ -12,8 +12,8 @@
 // waves cover up to four query heads of that kv head and 32 query rows each
 // (4 heads x 32 rows at GQA ratio 4, 2 x 64 at ratio 2, 1 x 128 without GQA),
 // so one K/V tile in LDS serves 128 (row, head) pairs.  Work items are ordered
-// sequence, then q tile (latest first: those rows see the most keys), then kv
-// head; workgroups go round-robin to the 8 XCDs, so with 8 | Hkv every XCD
+// sequence (longest first), then q tile (latest first: those rows see the most
+// keys), then kv head; workgroups go round-robin to the 8 XCDs, so with 8 | Hkv every XCD
 // serves one kv head, and the q tiles of a sequence run close together in
 // time on that XCD: the sequence's K/V for that head (and a shared prefix)
 // stay in the XCD's L2 instead of being read from HBM once per q tile.
@@ -332,7 +332,7 @@ __device__ __forceinline__ lds_bytes vslot_of(lds_bytes lbase, int t) {
 //
 // A work item is (sequence, q tile, kv head, head group).  A small plan
 // kernel lists the (sequence, q tile) pairs that hold at least one query row,
-// sequence by sequence and latest q tile first, as records carrying what a
+// sequence by sequence (longest first) and latest q tile first, as records carrying what a
 // workgroup needs to start on the pair; item i is pair i / ipp, kv head
 // (i % ipp) % Hkv, head group (i % ipp) / Hkv (ipp = Hkv * head_groups).
 // Items are dealt to eight queues, item i to queue i % 8, one queue per XCD:
