@@ -98,7 +98,10 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
                                   int32_t split_tokens);
 
 /* The number of context tokens one workgroup covers for these sizes when
- * split_tokens == 0 (automatic choice). */
+ * split_tokens == 0 (automatic choice): the whole context (max_context_len
+ * rounded up to 32) when one kv head's K and V of it fit in 512 KiB
+ * (max_context_len * head_dim <= 131072); otherwise a multiple of 256 in
+ * [256, 8192] that gives about 2048 workgroups. */
 int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len);
 

@@ -64,8 +64,8 @@ pkv_status check_block_size(int32_t block_size) {
   return PKV_OK;
 }
 
-int32_t resolve_split(int32_t batch, int32_t hq, int32_t hkv, int32_t max_ctx, int32_t split) {
-  return split > 0 ? split : pkv::decode_auto_split(batch, hq, hkv, max_ctx);
+int32_t resolve_split(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t max_ctx, int32_t split) {
+  return split > 0 ? split : pkv::decode_auto_split(batch, hq, hkv, d, max_ctx);
 }
 
 int32_t num_splits(int32_t max_ctx, int32_t split) {
@@ -143,10 +143,9 @@ pkv_status pkv_store_kvcache(const void* k, const void* v, void* k_cache, void* 
 
 int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len) {
-  (void)head_dim;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
     return 0;
-  return pkv::decode_auto_split(batch, num_q_heads, num_kv_heads, max_context_len);
+  return pkv::decode_auto_split(batch, num_q_heads, num_kv_heads, head_dim, max_context_len);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -156,7 +155,7 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
       max_context_len < 0 || split_tokens < 0 || num_q_heads % num_kv_heads)
     return SIZE_MAX;
   if (batch == 0) return 0;
-  const int32_t split = resolve_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
+  const int32_t split = resolve_split(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, split_tokens);
   const int32_t n = num_splits(max_context_len, split);
   if (n == 1) return 0;
   return static_cast<size_t>(batch) * num_q_heads * n * (head_dim + 2) * sizeof(float);
@@ -201,7 +200,7 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
                 num_kv_heads);
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t head_groups = (group + 15) / 16;
-  const int32_t split = resolve_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
+  const int32_t split = resolve_split(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, split_tokens);
   const int32_t n = num_splits(max_context_len, split);
   if (static_cast<int64_t>(batch) * num_kv_heads * head_groups * n > (int64_t{1} << 30))
     return fail(PKV_ERR_UNSUPPORTED, "more than 2^30 decode work items");

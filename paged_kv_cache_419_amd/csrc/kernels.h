@@ -41,7 +41,7 @@ struct DecodeArgs {
 };
 
 // Decode plan shared by the workspace query and the launch.
-int32_t decode_auto_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+int32_t decode_auto_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t max_context_len);
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -496,8 +496,14 @@ __global__ __launch_bounds__(D) void paged_decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
-int32_t decode_auto_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+int32_t decode_auto_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t max_context_len) {
+  // A context whose K and V for one kv head fit in 512 KiB (1024 tokens at
+  // head_dim 128, 2048 at 64) is never split: the split's second kernel costs
+  // more than the extra workgroups save (3-6 us per call at batches of 1-64,
+  // measured), while longer contexts at small batches gain from splitting.
+  if (static_cast<int64_t>(max_context_len) * head_dim <= 131072)
+    return max_context_len > 32 ? (max_context_len + 31) / 32 * 32 : 32;
   const int32_t group = num_q_heads / num_kv_heads;
   const int64_t pairs = static_cast<int64_t>(batch) * num_kv_heads * ((group + 15) / 16);
   // Aim for at least ~2048 workgroups (eight per CU) so the tail is short;

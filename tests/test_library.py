@@ -82,14 +82,20 @@ def test_decode_plan(lib):
     assert pkv.decode_workspace_bytes(0, 16, 8, 128, 1024) == 0
     with pytest.raises(pkv.PagedKVError):
         pkv.decode_workspace_bytes(4, 6, 4, 64, 100)
-    for args in [(256, 16, 8, 128, 1024), (512, 64, 8, 128, 32768), (4, 8, 2, 64, 700)]:
+    for args in [(256, 16, 8, 128, 1024), (512, 64, 8, 128, 32768), (4, 8, 2, 64, 700),
+                 (1, 16, 8, 128, 4096), (64, 8, 2, 64, 4096)]:
         split = pkv.decode_split_tokens(*args)
-        assert 256 <= split <= 8192 and split % 256 == 0
-    # whole sequences when there are enough (sequence, kv head) pairs to fill the chip
+        whole = split >= args[-1] and split % 32 == 0
+        assert whole or (256 <= split <= 8192 and split % 256 == 0)
+    # whole contexts while one kv head's K and V of a context fit in 512 KiB
     assert pkv.decode_split_tokens(256, 16, 8, 128, 1024) == 1024
-    # long contexts are cut into bounded pieces; tiny batches into single blocks
+    assert pkv.decode_split_tokens(4, 8, 2, 64, 700) == 704
+    assert pkv.decode_split_tokens(4, 8, 2, 64, 2048) == 2048
+    assert pkv.decode_workspace_bytes(4, 8, 2, 64, 700) == 0
+    # longer contexts are cut into bounded pieces; small batches into single blocks
     assert pkv.decode_split_tokens(512, 64, 8, 128, 32768) == 8192
-    assert pkv.decode_split_tokens(4, 8, 2, 64, 700) == 256
+    assert pkv.decode_split_tokens(1, 16, 8, 128, 4096) == 256
+    assert pkv.decode_split_tokens(4, 8, 2, 64, 2049) == 256
 
 
 def _prefill(lib, ns=2, tq=10, mq=5, mk=5, hq=4, hkv=2, d=64, bs=16, mb=1, causal=1, out=16,
