@@ -185,12 +185,26 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
     // 1024 samples in 64 evenly spaced runs of 16 consecutive entries: 64
     // cache lines per row (1024 lone entries would fetch 1024 lines)
     const int64_t sidx = static_cast<int64_t>(tid >> 4) * (V >> 6) + (tid & 15);
-    // The sample is loaded first and waited for by count (the batch's
-    // kSmUnroll loads may stay in flight): the load and its wait are written
-    // out, because the compiler would wait for every load before the first
-    // use of the sample.
-    float zs;
-    asm volatile("global_load_dword %0, %1, off" : "=v"(zs) : "v"(z + sidx) : "memory");
+    // The sample is loaded first, straight into skey (a direct-to-LDS load:
+    // it writes no register, so no register can be reused while it is in
+    // flight), and waited for by count, so the batch's kSmUnroll loads stay
+    // in flight: the compiler, waiting for a register load, would wait for
+    // the batch as well.  A wrong count would only let the threshold read a
+    // stale sample, which the exact selection below corrects.
+    {
+      const lds_bytes dst = (lds_bytes)skey + 4 * (tid & ~(kWave - 1));
+      const uint32_t lds_addr =  // the same for the whole wave
+          __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)));
+      uint32_t saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %2\n\t"
+          "global_load_lds_dword %1, off\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "v"(z + sidx), "s"(lds_addr)
+          : "memory");
+    }
     // Every wave's sample load goes out before any wave's batch loads (a
     // bare barrier: it orders the issue and waits for no memory), so the
     // samples do not queue behind 64 KiB of row data.
@@ -205,11 +219,11 @@ __global__ __launch_bounds__(kSmThreads) void topk_sample_kernel(SampleArgs a) {
     if (vec) {
 #pragma unroll
       for (int u = 0; u < kSmUnroll; ++u) first[u] = z4[min(tid + static_cast<int64_t>(u) * kSmThreads, n4 - 1)];
-      asm volatile("s_waitcnt vmcnt(4)" : "+v"(zs) : : "memory");
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     } else {
-      asm volatile("s_waitcnt vmcnt(0)" : "+v"(zs) : : "memory");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    skey[tid] = order_key(zs);
+    skey[tid] = order_key(__uint_as_float(skey[tid]));
     if (tid == 0) s_count = 0;
     const int64_t want = (static_cast<int64_t>(kSmThreads) * 4 * a.top_k + V - 1) / V + 4;
     const int s_rank = static_cast<int>(min<int64_t>(want, kSmThreads));
