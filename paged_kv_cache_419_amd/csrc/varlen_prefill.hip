@@ -358,8 +358,11 @@ constexpr int kWsRecsInt = kWsCountersInts + 16;       // first record (64-byte 
 constexpr uint32_t kXccIdReg = (31u << 11) | 20u;      // s_getreg: HW_REG_XCC_ID, 32 bits
 
 // Record of one (sequence, q tile) pair: sequence, q tile, first query row,
-// Lq, Lk, and the block-table entry of tile 0's rows for waves 0..3.
-enum : int { kRecSeq = 0, kRecQtile, kRecQstart, kRecLq, kRecLk, kRecBlk0 };
+// Lq, Lk, and the block-table entries of tile 0's and tile 1's rows for waves
+// 0..3 (so an item starts without reading the block table).
+enum : int { kRecSeq = 0, kRecQtile, kRecQstart, kRecLq, kRecLk, kRecBlk0, kRecBlk1 = kRecBlk0 + 4 };
+constexpr int kRecVecs = 4;  // 16-byte loads per record
+static_assert(kRecBlk1 + 4 <= kRecVecs * 4 && kRecVecs * 4 <= kRecInts, "record layout");
 
 struct PrefillSched {
   int* ws;               // workspace: queue counters, pair count, pair records
@@ -391,6 +394,7 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32
   __shared__ int s_order[kStaged];  // place -> sequence, when staged
   __shared__ int4 s_seq[kStaged];   // q start, Lq, Lk of each sequence, when staged
   __shared__ int4 s_blk[kStaged];   // block-table entries of key rows 0, 16, 32, 48
+  __shared__ int4 s_blk1[kStaged];  // and of rows 64, 80, 96, 112 (clamped to Lk - 1)
   __shared__ int s_total;
   const int tid = threadIdx.x;
   if (tid < kWsCountersInts) ws[tid] = 0;
@@ -404,11 +408,17 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32
     return int4{block_entry(a, s, 0 * kPfWaveRows), block_entry(a, s, 1 * kPfWaveRows),
                 block_entry(a, s, 2 * kPfWaveRows), block_entry(a, s, 3 * kPfWaveRows)};
   };
+  // tile 1's rows, clamped to the last key as the attention kernel's block lookup does
+  auto blk1_of = [&](int s, int lk) {
+    auto e = [&](int w) { return block_entry(a, s, min(kPfKeys + w * kPfWaveRows, max(lk - 1, 0))); };
+    return int4{e(0), e(1), e(2), e(3)};
+  };
   if (staged) {
     if (tid < a.num_seqs) {
       const int4 sq = seq_of(tid);
       s_seq[tid] = sq;
       s_blk[tid] = blk_of(tid);
+      s_blk1[tid] = blk1_of(tid, sq.z);
       s_incl[tid] = sq.z;
     }
     __syncthreads();
@@ -451,10 +461,12 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int32
       const int rank = r - (s_incl[lo] - first);
       const int4 sq = info(seq);
       const int4 bk = staged ? s_blk[seq] : blk_of(seq);
+      const int4 bk1 = staged ? s_blk1[seq] : blk1_of(seq, sq.z);
       int4* rec = reinterpret_cast<int4*>(ws + kWsRecsInt + static_cast<int64_t>(base + r) * kRecInts);
       rec[0] = int4{seq, first - 1 - rank, sq.x, sq.y};
       rec[1] = int4{sq.z, bk.x, bk.y, bk.z};
-      rec[2] = int4{bk.w, 0, 0, 0};
+      rec[2] = int4{bk.w, bk1.x, bk1.y, bk1.z};
+      rec[3] = int4{bk1.w, 0, 0, 0};
     }
     __syncthreads();
     if (tid == 0) s_total = base + chunk;
@@ -485,17 +497,18 @@ __device__ int claim_item(int* counters, int n_items, int q0, int ticket) {
 struct Item {
   int seq, qtile, q_start, lq, lk, g, hg;
   int64_t blk0;  // block of this wave's rows of tile 0
+  int32_t blk1;  // and of tile 1
 };
 
 // Every lane reads the same record (one request per wave), then the fields
 // are made wave-uniform.
-__device__ __forceinline__ void load_record(const int* ws, int pair, u32x4 (&r)[3]) {
+__device__ __forceinline__ void load_record(const int* ws, int pair, u32x4 (&r)[kRecVecs]) {
   const int* p = ws + kWsRecsInt + static_cast<int64_t>(pair) * kRecInts;
 #pragma unroll
-  for (int i = 0; i < 3; ++i) r[i] = ldg16(p + 4 * i);
+  for (int i = 0; i < kRecVecs; ++i) r[i] = ldg16(p + 4 * i);
 }
 
-__device__ __forceinline__ Item item_of(const PrefillSched& sc, int id, const u32x4 (&r)[3], int wave,
+__device__ __forceinline__ Item item_of(const PrefillSched& sc, int id, const u32x4 (&r)[kRecVecs], int wave,
                                         int ipp) {
   Item it;
   const int rem = id % ipp;
@@ -511,6 +524,8 @@ __device__ __forceinline__ Item item_of(const PrefillSched& sc, int id, const u3
   const int b = wave == 0 ? f(kRecBlk0) : wave == 1 ? f(kRecBlk0 + 1) : wave == 2 ? f(kRecBlk0 + 2)
                                                                                    : f(kRecBlk0 + 3);
   it.blk0 = b;
+  it.blk1 = wave == 0 ? f(kRecBlk1) : wave == 1 ? f(kRecBlk1 + 1) : wave == 2 ? f(kRecBlk1 + 2)
+                                                                              : f(kRecBlk1 + 3);
   return it;
 }
 
@@ -617,7 +632,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
 
   Item cur;
   WaveState<D> w;
-  u32x4 rec[3];
+  u32x4 rec[kRecVecs];
   {
     load_record(sc.ws, first_id / ipp, rec);
     cur = item_of(sc, first_id, rec, wave, ipp);
@@ -671,7 +686,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
         barrier_after_vm<0>();
       }
     };
-    int32_t blk_next = n_eff > 1 ? tile_block(sv, kPfKeys, wave) : 0;
+    int32_t blk_next = n_eff > 1 ? cur.blk1 : 0;  // tile 1's block, from the record
     auto inner_step = [&](int t) -> DmaJob {  // loads of tile t + 1
       sync_step(t);
       return dma_job<D>(sv, blk_next, (t + 1) * kPfKeys, wave, t + 1 < n_tiles, kslot(T + 1), vslot(T + 1));
@@ -700,7 +715,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void varlen_prefill_kernel(PrefillAr
     sync_step(t);
     // Every word of the record stays allocated until here (no other value
     // may take a register a record load still writes).
-    asm volatile("" ::"v"(rec[0]), "v"(rec[1]), "v"(rec[2]));
+    asm volatile("" ::"v"(rec[0]), "v"(rec[1]), "v"(rec[2]), "v"(rec[3]));
     const bool has_next = nxt_id >= 0;
     const Item nx = item_of(sc, max(nxt_id, 0), rec, wave, ipp);
     u32x4 qn[S::KS];
