@@ -125,8 +125,8 @@ int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_
  *   max_context_len  host-side bound: context_lens[b] <= max_context_len <=
  *                 max_blocks_per_seq * block_size (sizes the launch; no device
  *                 read).  Tokens beyond it are never visited.  Workgroups take
- *                 the sequences longest first (the result does not depend on
- *                 the order).
+ *                 the sequences longest first in batches of up to 2048 (the
+ *                 result does not depend on the order).
  *   split_tokens  context tokens per workgroup: 0 = automatic, else a positive
  *                 multiple of 32.  Sequences longer than one split are
  *                 processed in several workgroups whose partial softmax states

@@ -236,6 +236,9 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
   a.split_tokens = split;
   a.n_split = n;
   a.max_context_len = max_context_len;
+  // every workgroup reads all of context_lens to find its place: kept to
+  // batches whose lengths fit a few per thread
+  a.work_order = batch <= 2048 ? 1 : 0;
   a.order_shift = 0;
   while ((max_context_len >> a.order_shift) > 255) ++a.order_shift;
   a.scale_log2 = scale * 1.4426950408889634f;

@@ -28,6 +28,7 @@ struct DecodeArgs {
   int32_t split_tokens;
   int32_t n_split;
   int32_t max_context_len;
+  int32_t work_order;   // 1: sequences longest first (batches up to 2048), 0: batch order
   int32_t order_shift;  // max_context_len >> order_shift < 256: length classes of the work order
   float scale_log2;     // scale * log2(e)
   // Fused store (all null / 0 otherwise): the new token of sequence b is row b

@@ -302,8 +302,8 @@ __device__ SeqPick sequence_in_work_order(const DecodeArgs& a, int r) {
   return SeqPick{pick[2], pick[3]};
 }
 
-template <int D>
 // (second bound: at least two waves per SIMD, i.e. up to 256 registers per lane)
+template <int D>
 __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs a) {
   using S = DecodeShape<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS];
@@ -315,13 +315,17 @@ __global__ __launch_bounds__(kDecThreads, 2) void paged_decode_kernel(DecodeArgs
   // order, where one sequence's kv heads run side by side.  Within a kv head
   // the sequences go longest first (sequence_in_work_order): 6 % faster at
   // 256 contexts of 100-1024 tokens and 4 % at 512 of 4k-32k tokens than
-  // batch order.
+  // batch order.  Batches above 2048 sequences keep batch order (each
+  // workgroup would read all of context_lens).
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.head_groups;
   const int64_t lin = blockIdx.x;
   const int split = static_cast<int>(lin / pairs);
   const int64_t pair = lin - split * pairs;
   const int gy = static_cast<int>(pair / a.batch);
-  const SeqPick sp = sequence_in_work_order(a, static_cast<int>(pair % a.batch));
+  const int place = static_cast<int>(pair % a.batch);
+  const SeqPick sp = a.work_order
+                         ? sequence_in_work_order(a, place)
+                         : SeqPick{place, min(max(a.context_lens[place], 0), a.max_context_len)};
   const int b = __builtin_amdgcn_readfirstlane(sp.b);
   const int g = gy / a.head_groups;
   const int hg = gy - g * a.head_groups;

@@ -83,10 +83,14 @@ def small_workloads():
         head_dim=64, block_size=16, seed=28, name="decode_b513")
     # batches past 1024 sequences: the decode work order keeps at most four lengths per
     # thread in registers and reads the rest again (five per thread here, many equal
-    # lengths); the prefill plan lists more than 1024 sequences in batch order
+    # lengths), past 2048 decode keeps batch order; the prefill plan lists more than 1024
+    # sequences in batch order
     cases["decode_b1100"] = W.decode(
         rng.choice([0, 1, 3, 16, 17, 40], size=1100).tolist(), num_q_heads=2, num_kv_heads=1,
         head_dim=64, block_size=16, seed=29, name="decode_b1100")
+    cases["decode_b2100"] = W.decode(
+        rng.choice([0, 1, 2, 5, 33], size=2100).tolist(), num_q_heads=1, num_kv_heads=1,
+        head_dim=64, block_size=16, seed=31, name="decode_b2100")
     cases["prefill_s1030"] = W.prefill(
         rng.integers(0, 6, size=1030, endpoint=True).tolist(), num_q_heads=2, num_kv_heads=1,
         head_dim=64, block_size=16, seed=30, name="prefill_s1030")
