@@ -383,7 +383,7 @@ __device__ __forceinline__ int32_t block_entry(const PrefillArgs& a, int seq, in
 // clears the queue counters.  Batches of up to 1024 sequences are listed
 // longest first (by key count, ties in batch order), each sequence's q tiles
 // together: the long items start first and short ones fill the end of the
-// launch (~1.5 % faster at 64 sequences of 100-1024 tokens than batch
+// launch (~1 % faster at 64 sequences of 100-1024 tokens than batch
 // order); their cu_seqlens and block-table entries are read once, all at
 // the start, into LDS.  Larger batches keep batch order and read them where
 // they are needed.
