@@ -101,7 +101,8 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  * split_tokens == 0 (automatic choice): the whole context (max_context_len
  * rounded up to 32) when one kv head's K and V of it fit in 512 KiB
  * (max_context_len * head_dim <= 131072); otherwise a multiple of 256 in
- * [256, 8192] that gives about 2048 workgroups. */
+ * [256, 32768] that gives about 2048 workgroups.  Pieces of 4096 tokens or
+ * more over at least 2048 workgroups run one workgroup per CU. */
 int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len);
 

@@ -512,11 +512,14 @@ int32_t decode_auto_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_hea
   const int64_t pairs = static_cast<int64_t>(batch) * num_kv_heads * ((group + 15) / 16);
   // Aim for at least ~2048 workgroups (eight per CU) so the tail is short;
   // never split below 256 tokens and never let one workgroup walk more than
-  // kMaxSplit tokens (long contexts then spread over many CUs).  At 512
-  // contexts of 4k-32k tokens, pieces of 8192 tokens beat 4096 by ~1.3 %
-  // (fewer workgroup starts, half the partial results) and 16384 gains no more.
+  // kMaxSplit tokens (longer contexts then spread over several CUs).  Long
+  // pieces run one workgroup per CU (launch_paged_decode), where fewer, longer
+  // pieces stream best: at 512 contexts of 4k-32k tokens whole contexts take
+  // 2.5 % less time than 8192-token pieces, and at 64-256 such contexts the
+  // rule below is 2-4 % faster than pieces capped at 8192 with two workgroups
+  // per CU (measured).
   constexpr int64_t kWantWGs = 2048;
-  constexpr int64_t kMaxSplit = 8192;
+  constexpr int64_t kMaxSplit = 32768;
   int64_t n = pairs > 0 ? (kWantWGs + pairs - 1) / pairs : 1;
   if (n < 1) n = 1;
   int64_t split = (static_cast<int64_t>(max_context_len) + n - 1) / n;
@@ -526,14 +529,29 @@ int32_t decode_auto_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_hea
   return static_cast<int32_t>(split);
 }
 
+// LDS a decode workgroup asks for when it is to run alone on its CU: more
+// than half of the CU's 160 KiB, so a second one cannot be resident.
+constexpr uint32_t kOnePerCuLds = 96 * 1024;
+static_assert(DecodeShape<128>::LDS < kOnePerCuLds && DecodeShape<64>::LDS < kOnePerCuLds, "LDS pad");
+
 hipError_t launch_paged_decode(const DecodeArgs& args, hipStream_t stream) {
   const DecodeArgs& a = args;
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.n_split) * a.num_kv_heads *
                                         a.head_groups * a.batch));
+  // Pieces of 4096 tokens and more, over a grid of at least 2048 workgroups
+  // (eight rounds of the CUs), run one workgroup per CU: the long streams
+  // then go 1.6-4 % faster than with two per CU (measured at 64-512 contexts
+  // of 4k-32k tokens).  Short pieces keep two per CU, which they need to hide
+  // their start-up latency (256 contexts of 100-1024 tokens take 15 % longer
+  // at one).  The extra dynamic LDS is never touched; it only keeps a second
+  // workgroup off the CU.
+  const bool one_per_cu = a.split_tokens >= 4096 && grid.x >= 2048;
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL(paged_decode_kernel<128>, grid, dim3(kDecThreads), 0, stream, a);
+    const uint32_t pad = one_per_cu ? kOnePerCuLds - DecodeShape<128>::LDS : 0;
+    hipLaunchKernelGGL(paged_decode_kernel<128>, grid, dim3(kDecThreads), pad, stream, a);
   } else {
-    hipLaunchKernelGGL(paged_decode_kernel<64>, grid, dim3(kDecThreads), 0, stream, a);
+    const uint32_t pad = one_per_cu ? kOnePerCuLds - DecodeShape<64>::LDS : 0;
+    hipLaunchKernelGGL(paged_decode_kernel<64>, grid, dim3(kDecThreads), pad, stream, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.n_split == 1) return err;

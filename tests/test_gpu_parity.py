@@ -241,3 +241,22 @@ def test_full_size(name, strata, oracle_pool):
     assert torch.isfinite(out.float()).all()
     _within_visible_v_range(w, t, out)
     _note(f"full size {name}: every row within the range of its visible V rows")
+
+
+def test_decode_long_pieces_one_per_cu(oracle_pool):
+    """Pieces of 4096 tokens over 2048 workgroups: the launch that keeps one workgroup
+    per CU, with the split combine behind it; every row against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(4242))
+    ctx = rng.integers(4097, 6000, size=128, endpoint=True)
+    w = W.decode(ctx.tolist(), num_q_heads=8, num_kv_heads=8, head_dim=64, block_size=256,
+                 id_mode="choice", max_blocks_per_seq=24, seed=37, rng=rng,
+                 name="decode_long_pieces")
+    _note("decode long pieces: 128 contexts of 4097-6000 tokens, split 4096, 2048 workgroups")
+    t, out = H.gpu_step(w, split_tokens=4096)
+    seqs = list(range(w.num_seqs))
+    bits = bf16_bits(out)
+    rows = [bits[H.rows_for(w, [s])] for s in seqs]
+    n_rows, n_bad, ea, er, first_bad = oracle_pool.compare(w, seqs, rows)
+    _note(f"decode long pieces: {n_rows} rows, max abs err {ea:.3e}, max rel err {er:.3e}")
+    assert n_rows == w.num_seqs
+    assert n_bad == 0, f"{n_bad} elements outside tolerance (first in sequence {first_bad})"

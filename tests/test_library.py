@@ -86,14 +86,15 @@ def test_decode_plan(lib):
                  (1, 16, 8, 128, 4096), (64, 8, 2, 64, 4096)]:
         split = pkv.decode_split_tokens(*args)
         whole = split >= args[-1] and split % 32 == 0
-        assert whole or (256 <= split <= 8192 and split % 256 == 0)
+        assert whole or (256 <= split <= 32768 and split % 256 == 0)
     # whole contexts while one kv head's K and V of a context fit in 512 KiB
     assert pkv.decode_split_tokens(256, 16, 8, 128, 1024) == 1024
     assert pkv.decode_split_tokens(4, 8, 2, 64, 700) == 704
     assert pkv.decode_split_tokens(4, 8, 2, 64, 2048) == 2048
     assert pkv.decode_workspace_bytes(4, 8, 2, 64, 700) == 0
     # longer contexts are cut into bounded pieces; small batches into single blocks
-    assert pkv.decode_split_tokens(512, 64, 8, 128, 32768) == 8192
+    assert pkv.decode_split_tokens(512, 64, 8, 128, 32768) == 32768
+    assert pkv.decode_split_tokens(64, 64, 8, 128, 32216) == 8192
     assert pkv.decode_split_tokens(1, 16, 8, 128, 4096) == 256
     assert pkv.decode_split_tokens(4, 8, 2, 64, 2049) == 256
 
