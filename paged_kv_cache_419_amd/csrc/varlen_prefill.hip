@@ -234,6 +234,14 @@ __device__ __forceinline__ float row_max_scaled(const f32x16 (&s)[kPfKB], float 
 // once right after the barrier.  The first V^T operands are read before the
 // softmax, so their latency hides behind it, and the rest stay kVAhead MFMAs
 // ahead of the PV product.
+//
+// Wave priority: a wave issuing MFMAs is raised above one doing softmax
+// arithmetic (2 during the S product, 3 during the PV product, 0 otherwise),
+// so that when both waves of a SIMD have an instruction ready the matrix
+// core is fed first and the other wave's VALU work fills its busy cycles.
+// Measured 4-5 % faster on the prefix workload and 2.5-3 % on the varlen one
+// than equal priorities (other levels, 1/3 or 3/3 or raising the softmax to
+// 1, were within noise of this).
 template <int D>
 __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_bytes vt,
                                              const uint32_t (&kaddr)[PrefillShape<D>::KS],
@@ -265,6 +273,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
   f32x16 s[kPfKB];
 #pragma unroll
   for (int i = 0; i < kReadAhead; ++i) kread(i);
+  __builtin_amdgcn_s_setprio(2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kNS; ++i) {
@@ -276,6 +285,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
   }
 #pragma unroll
   for (int j = 0; j < kVAhead; ++j) vread(j);
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 
   // element 4j + i of s[kb] is key k0 + 32 kb + 8 j + 4 h + i of this lane's row
@@ -307,6 +317,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
     tsum = tile_weights(s, pb, w.m, c);
   }
   w.lsum += tsum;
+  __builtin_amdgcn_s_setprio(3);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kNP; ++j) {
@@ -315,6 +326,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
     w.o[cb] = mfma32x32x16(u32x4{vlo[j].x, vlo[j].y, vhi[j].x, vhi[j].y}, pb[u], w.o[cb]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // LDS slot of ring position t: a K tile followed by a V tile.
