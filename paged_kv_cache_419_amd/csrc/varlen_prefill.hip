@@ -255,7 +255,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D>& w, lds_bytes kt, lds_
   constexpr int kNP = kPfU * S::DC;   // MFMAs of the PV product
   constexpr int kGap = kNS / (2 * S::LOADS);
   static_assert(kGap >= 1 && kGap * 2 * S::LOADS == kNS, "loads per MFMA slot");
-  constexpr int kReadAhead = 3;
+  // (4 is ~1 % faster than 3 on the prefix workload with the wave priorities;
+  // 2, 5 and V read-aheads of 2, 6 or 8 were no better)
+  constexpr int kReadAhead = 4;
   constexpr int kVAhead = 4;
   static_assert(kReadAhead < kNS && kVAhead <= kNP, "read-ahead depth");
 
