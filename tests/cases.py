@@ -65,6 +65,15 @@ def small_workloads():
     cases["decode_bigscale"] = W.decode([190, 700, 5], num_q_heads=4, num_kv_heads=2,
                                         head_dim=128, block_size=16, seed=24, scale=3.0,
                                         name="decode_bigscale")
+    # blocks larger than the default: full (non-causal) prefill at head_dim 128 and GQA
+    # ratio 8 over 128-token blocks, with history; decode over 1024-token blocks with
+    # contexts on both sides of a block boundary
+    cases["prefill_full_d128_g8_bs128"] = W.prefill(
+        [70, 130, 1], hist=[0, 200, 50], num_q_heads=16, num_kv_heads=2, head_dim=128,
+        block_size=128, seed=32, causal=False, name="prefill_full_d128_g8_bs128")
+    cases["decode_bs1024"] = W.decode([1, 1023, 1024, 1025, 2500], num_q_heads=8, num_kv_heads=2,
+                                      head_dim=128, block_size=1024, seed=33,
+                                      name="decode_bs1024")
     # batches whose (sequence, kv head) items outnumber the resident workgroups several
     # times over: many equal contexts, empty contexts, head groups of 16 with two groups
     # per kv head, and batches of 512 and 513 sequences

@@ -83,7 +83,7 @@ def test_store_skips_slots_past_the_cache():
 
 @pytest.mark.parametrize("split", [32, 64, 128, 256, 2048])
 @pytest.mark.parametrize("name", ["decode_edge_b4", "decode_tiny_bs16", "decode_g16",
-                                  "decode_long_b512[2]"])
+                                  "decode_long_b512[2]", "decode_bs1024"])
 def test_decode_splits(name, split):
     _note(f"decode {name} split {split}")
     w = cases.get(name)
