@@ -22,7 +22,10 @@
 // slot row (64-bit, in scalar registers) and whose size is the number of live
 // tokens in the half: lanes of tokens past the context read zeros from the
 // hardware range check, never the stale (possibly NaN) contents of unused
-// slots.  Per-lane offsets are constant for the whole loop.
+// slots.  Per-lane offsets are constant for the whole loop.  Two workgroups
+// are resident per CU, which short contexts need to hide each workgroup's
+// start-up; long pieces of work run one per CU, where they stream faster
+// (launch_paged_decode).
 //
 // Matrix cores.  Scores are computed transposed, S^T[token][head] = K Q^T, on
 // 16x16x32 bf16 MFMA tiles: K rows go straight from HBM into the A operand,
