@@ -33,6 +33,8 @@
 // exchange per tile, and the probabilities already sit in the B-operand layout
 // of O^T[d][row] += V^T P^T, whose V^T operand comes from ds_read_b64_tr_b16.
 // fp32 accumulation; probabilities are rounded to bf16 for the second product.
+// A wave raises its priority while it issues MFMAs, so that of the two waves
+// sharing a SIMD the one feeding the matrix core goes first (compute_tile).
 #include "common.h"
 #include "kernels.h"
 
