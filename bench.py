@@ -668,7 +668,9 @@ def measure(name, args, torch, pkv, dev, pool, cpu_budget):
 
 
 HEADLINE = "decode_long_b512"  # the largest single-GPU workload (38.7 GB of K/V per step)
-SUB_WORKLOADS = ("decode_b256", "prefill_varlen_s64", "prefill_prefix_s128", "decode_edge_b4")
+# the other configurations, then one GPU's share of the headline under 8-way tensor parallelism
+SUB_WORKLOADS = ("decode_b256", "prefill_varlen_s64", "prefill_prefix_s128", "decode_edge_b4",
+                 "decode_long_b512_shard8")
 
 
 def main():

@@ -203,9 +203,10 @@ def oracle_pool():
 
 
 # every sequence of the first four workloads; a 32-bin stratified sample of the
-# 512 long contexts (the oracle regenerates each one's 4k-32k positions on the host)
+# 512 long contexts (the oracle regenerates each one's 4k-32k positions on the host),
+# for the long decode and for its tensor-parallel shard
 FULL = [("decode_edge_b4", None), ("decode_b256", None), ("prefill_varlen_s64", None),
-        ("prefill_prefix_s128", None), ("decode_long_b512", 32)]
+        ("prefill_prefix_s128", None), ("decode_long_b512", 32), ("decode_long_b512_shard8", 32)]
 
 
 @pytest.mark.parametrize("name,strata", FULL)

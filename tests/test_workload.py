@@ -52,6 +52,10 @@ def test_published_shapes():
     assert c5.num_seqs == 512 and 4096 <= c5.lk.min() and c5.lk.max() <= 32768
     demand = sum(oracle.blocks_for(int(n), 256) for n in c5.lk)
     assert c5.num_blocks == int(np.ceil(1.1 * demand))
+    # one tensor-parallel shard of c5: its lengths and tables, one kv head and its 8 query heads
+    sh = W.make("decode_long_b512_shard8")
+    assert (sh.lk == c5.lk).all() and (sh.block_tables == c5.block_tables).all()
+    assert (sh.num_q_heads, sh.num_kv_heads, sh.head_dim) == (8, 1, 128)
 
 
 def test_deterministic():

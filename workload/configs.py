@@ -1,4 +1,5 @@
-"""The five seeded workloads of the paged KV-cache data plane, by name.
+"""The seeded workloads of the paged KV-cache data plane, by name: the five
+configurations and one tensor-parallel shard of the long decode.
 
 Draw order for every workload: lengths first, then physical block ids, from one
 ``numpy.random.Generator(PCG64(seed))``; Q/K/V values are counter-based
@@ -21,6 +22,10 @@ WORKLOADS = {
     "prefill_varlen_s64": (4193, "causal varlen prefill, 64 seqs, length U[100,1024], Hq 32 / Hkv 8, d 128"),
     "prefill_prefix_s128": (4194, "prefix-cached prefill, 128 seqs, 2048 shared + U[64,512], Hq 32 / Hkv 8, d 128"),
     "decode_long_b512": (4195, "long decode, batch 512, context U[4096,32768], Hq 64 / Hkv 8, d 128"),
+    # one GPU's share of the long decode under tensor parallelism over its 8 kv heads: the same
+    # seed, so the same context lengths and block tables, at Hq 8 / Hkv 1
+    "decode_long_b512_shard8": (4195, "long decode at one of 8 tensor-parallel shards: batch 512, "
+                                      "context U[4096,32768], Hq 8 / Hkv 1, d 128"),
 }
 
 
@@ -50,9 +55,10 @@ def make(name: str, seed: int | None = None) -> synth.Workload:
                              block_size=BLOCK, id_mode="choice",
                              max_blocks_per_seq=2048 // BLOCK + 512 // BLOCK, seed=seed,
                              rng=rng, name=name)
-    if name == "decode_long_b512":
+    if name in ("decode_long_b512", "decode_long_b512_shard8"):
         ctx = rng.integers(4096, 32768, size=512, endpoint=True)
-        return synth.decode(ctx, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=BLOCK,
+        hq, hkv = (64, 8) if name == "decode_long_b512" else (8, 1)
+        return synth.decode(ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=BLOCK,
                             id_mode="choice", max_blocks_per_seq=32768 // BLOCK, seed=seed,
                             rng=rng, name=name)
     raise AssertionError(name)
